@@ -1,0 +1,215 @@
+"""ctypes binding of libfp8dq.so: argument marshalling only.
+
+Every function here has the name of a C entry point in include/fp8dq.h,
+takes torch tensors (device memory) and passes their pointers, sizes and
+the current HIP stream to the library. All arithmetic runs in the library's
+HIP kernels; there is no other implementation to fall back to, and a missing
+library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfp8dq.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "fp8dq.h")
+
+AUTO, FORCE_PREFILL, FORCE_DECODE = 0, 1, 2
+DECODE_MAX_M = 64
+GROUP = 128
+
+_c_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_SIGS = {
+    "fp8_quant_act": (ctypes.c_int, [_c_p, _i64, _i64, ctypes.c_int32, _c_p, _c_p, _c_p]),
+    "fp8_quant_weight_block": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p]),
+    "fp8_gemm": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64,
+                                ctypes.c_uint32, _c_p, ctypes.c_size_t, _c_p]),
+    "fp8_gemm_block": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64,
+                                      ctypes.c_uint32, _c_p, ctypes.c_size_t, _c_p]),
+    "fp8_linear": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _c_p, _c_p,
+                                  ctypes.c_uint32, _c_p, ctypes.c_size_t, _c_p]),
+    "fp8_linear_block": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _c_p,
+                                        _c_p, ctypes.c_uint32, _c_p, ctypes.c_size_t, _c_p]),
+    "fp8_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, ctypes.c_int32, ctypes.c_uint32]),
+    "fp8_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "fp8dq_version": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class Fp8dqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({status_text(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m fp8_dynamic_quantized_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/fp8dq.h declares."""
+    text = open(HEADER).read()
+    return re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, re.M)
+
+
+def status_text(status: int) -> str:
+    return lib().fp8_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise Fp8dqError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream):
+    import torch
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, dtype, shape, name):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)}, got "
+                         f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be device memory")
+
+
+def fp8_workspace_bytes(M: int, N: int, K: int, block: bool = False,
+                        flags: int = AUTO) -> int:
+    return int(lib().fp8_workspace_bytes(M, N, K, int(block), flags))
+
+
+def fp8_status_string(status: int) -> str:
+    return status_text(status)
+
+
+def fp8dq_version() -> str:
+    return lib().fp8dq_version().decode()
+
+
+def fp8_quant_act(x, group: int = 0, q=None, scale=None, stream=None):
+    """Quantize bf16 x [rows, K] -> (codes uint8 [rows, K], scales fp32)."""
+    import torch
+    rows, K = x.shape
+    _need(x, torch.bfloat16, (rows, K), "x")
+    sshape = (rows,) if group == 0 else (rows, K // GROUP)
+    q = torch.empty((rows, K), dtype=torch.uint8, device=x.device) if q is None else q
+    scale = torch.empty(sshape, dtype=torch.float32, device=x.device) if scale is None else scale
+    _check("fp8_quant_act", lib().fp8_quant_act(
+        _ptr(x), rows, K, group, _ptr(q), _ptr(scale), _stream(x, stream)))
+    return q, scale
+
+
+def fp8_quant_weight_block(w, qw=None, sw=None, stream=None):
+    """128x128 block quantization of bf16 w [N, K] -> (codes, sw [N/128, K/128])."""
+    import torch
+    N, K = w.shape
+    _need(w, torch.bfloat16, (N, K), "w")
+    qw = torch.empty((N, K), dtype=torch.uint8, device=w.device) if qw is None else qw
+    sw = torch.empty((N // GROUP, K // GROUP), dtype=torch.float32,
+                     device=w.device) if sw is None else sw
+    _check("fp8_quant_weight_block", lib().fp8_quant_weight_block(
+        _ptr(w), N, K, _ptr(qw), _ptr(sw), _stream(w, stream)))
+    return qw, sw
+
+
+def _workspace(M, N, K, block, flags, ws, device):
+    import torch
+    need = fp8_workspace_bytes(M, N, K, block, flags)
+    if need and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    return ws, nbytes
+
+
+def fp8_gemm(qx, sx, qw, sw, y=None, flags: int = AUTO, ws=None, stream=None):
+    """y = bf16((qx qw^T) * sx[m] * sw[n]); codes uint8, scales fp32."""
+    import torch
+    M, K = qx.shape
+    N = qw.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=qx.device) if y is None else y
+    ws, nb = _workspace(M, N, K, False, flags, ws, qx.device)
+    _check("fp8_gemm", lib().fp8_gemm(
+        _ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(y), M, N, K, flags,
+        _ptr(ws), nb, _stream(qx, stream)))
+    return y
+
+
+def fp8_gemm_block(qx, sx, qw, sw, y=None, flags: int = AUTO, ws=None, stream=None):
+    """Block-scaled GEMM: sx [M, K/128], sw [N/128, K/128]."""
+    import torch
+    M, K = qx.shape
+    N = qw.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=qx.device) if y is None else y
+    ws, nb = _workspace(M, N, K, True, flags, ws, qx.device)
+    _check("fp8_gemm_block", lib().fp8_gemm_block(
+        _ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(y), M, N, K, flags,
+        _ptr(ws), nb, _stream(qx, stream)))
+    return y
+
+
+def fp8_linear(x, qw, sw, y=None, qx_out=None, sx_out=None, flags: int = AUTO,
+               ws=None, stream=None):
+    """FP8-Dynamic linear: per-token quantization of x, then the FP8 GEMM.
+
+    Returns (y bf16 [M, N], qx uint8 [M, K], sx fp32 [M]).
+    """
+    import torch
+    M, K = x.shape
+    N = qw.shape[0]
+    _need(x, torch.bfloat16, (M, K), "x")
+    dev = x.device
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    qx_out = torch.empty((M, K), dtype=torch.uint8, device=dev) if qx_out is None else qx_out
+    sx_out = torch.empty((M,), dtype=torch.float32, device=dev) if sx_out is None else sx_out
+    ws, nb = _workspace(M, N, K, False, flags, ws, dev)
+    _check("fp8_linear", lib().fp8_linear(
+        _ptr(x), _ptr(qw), _ptr(sw), _ptr(y), M, N, K, _ptr(qx_out), _ptr(sx_out),
+        flags, _ptr(ws), nb, _stream(x, stream)))
+    return y, qx_out, sx_out
+
+
+def fp8_linear_block(x, qw, sw, y=None, qx_out=None, sx_out=None,
+                     flags: int = AUTO, ws=None, stream=None):
+    """Block variant: group-128 activation quantization, block-scaled GEMM.
+
+    Returns (y bf16 [M, N], qx uint8 [M, K], sx fp32 [M, K/128]).
+    """
+    import torch
+    M, K = x.shape
+    N = qw.shape[0]
+    _need(x, torch.bfloat16, (M, K), "x")
+    dev = x.device
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    qx_out = torch.empty((M, K), dtype=torch.uint8, device=dev) if qx_out is None else qx_out
+    sx_out = (torch.empty((M, K // GROUP), dtype=torch.float32, device=dev)
+              if sx_out is None else sx_out)
+    ws, nb = _workspace(M, N, K, True, flags, ws, dev)
+    _check("fp8_linear_block", lib().fp8_linear_block(
+        _ptr(x), _ptr(qw), _ptr(sw), _ptr(y), M, N, K, _ptr(qx_out), _ptr(sx_out),
+        flags, _ptr(ws), nb, _stream(x, stream)))
+    return y, qx_out, sx_out

@@ -1,0 +1,190 @@
+// C-ABI boundary of the FP8-Dynamic linear library (see include/fp8dq.h).
+// Every argument is checked here, on the host, before anything is enqueued.
+#include "fp8dq.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+
+namespace {
+
+using fp8dq::DecodePlan;
+
+inline bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? FP8DQ_OK : FP8DQ_ERR_HIP;
+}
+
+inline bool known_flags(uint32_t f) {
+  return f == FP8DQ_AUTO || f == FP8DQ_FORCE_PREFILL || f == FP8DQ_FORCE_DECODE;
+}
+
+inline bool use_decode(int64_t M, uint32_t flags) {
+  if (flags == FP8DQ_FORCE_DECODE) return true;
+  if (flags == FP8DQ_FORCE_PREFILL) return false;
+  return M <= FP8DQ_DECODE_MAX_M;
+}
+
+// Workspace for a GEMM call: the decode path processes M in slabs of at
+// most 64 rows (one after another on the stream), so one slab's partials.
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, uint32_t flags) {
+  if (M <= 0 || N <= 0 || K <= 0 || (K % 128) != 0) return 0;
+  if (!use_decode(M, flags)) return 0;
+  const int64_t slab = M < FP8DQ_DECODE_MAX_M ? M : FP8DQ_DECODE_MAX_M;
+  const DecodePlan p = fp8dq::plan_decode(slab, N, K);
+  return fp8dq::decode_workspace_bytes(slab, N, p);
+}
+
+int check_gemm_args(const uint8_t* qx, const float* sx, const uint8_t* qw,
+                    const float* sw, const void* y, int64_t M, int64_t N,
+                    int64_t K, uint32_t flags, const void* ws, size_t ws_bytes,
+                    bool block) {
+  if (M < 0 || N < 0 || K <= 0 || (K % 128) != 0) return FP8DQ_ERR_SHAPE;
+  if (block && (N % 128) != 0) return FP8DQ_ERR_SHAPE;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return FP8DQ_ERR_SHAPE;
+  if (!known_flags(flags)) return FP8DQ_ERR_FLAGS;
+  if (M == 0 || N == 0) return FP8DQ_OK;
+  if (!qx || !sx || !qw || !sw || !y) return FP8DQ_ERR_NULL;
+  if (!aligned16(qx) || !aligned16(sx) || !aligned16(qw) || !aligned16(sw) ||
+      !aligned16(y))
+    return FP8DQ_ERR_ALIGN;
+  const size_t need = gemm_ws_bytes(M, N, K, flags);
+  if (need > 0) {
+    if (!ws) return FP8DQ_ERR_NULL;
+    if (!aligned16(ws)) return FP8DQ_ERR_ALIGN;
+    if (ws_bytes < need) return FP8DQ_ERR_WORKSPACE;
+  }
+  return FP8DQ_OK;
+}
+
+// Launch a validated GEMM (M, N > 0).
+int run_gemm(const uint8_t* qx, const float* sx, const uint8_t* qw,
+             const float* sw, void* y, int64_t M, int64_t N, int64_t K,
+             uint32_t flags, void* ws, bool block, hipStream_t st) {
+  if (!use_decode(M, flags)) {
+    fp8dq::launch_gemm_prefill(qx, sx, qw, sw, y, M, N, K, block, st);
+    return launch_status();
+  }
+  const int64_t G = K / 128;
+  for (int64_t m0 = 0; m0 < M; m0 += FP8DQ_DECODE_MAX_M) {
+    const int64_t rows = (M - m0) < FP8DQ_DECODE_MAX_M ? (M - m0) : FP8DQ_DECODE_MAX_M;
+    const DecodePlan p = fp8dq::plan_decode(rows, N, K);
+    const float* sxs = sx + (block ? m0 * G : m0);
+    fp8dq::launch_gemm_decode(qx + m0 * K, sxs, qw, sw,
+                              static_cast<uint16_t*>(y) + m0 * N,
+                              static_cast<float*>(ws), rows, N, K, block, p, st);
+    const int s = launch_status();
+    if (s != FP8DQ_OK) return s;
+  }
+  return FP8DQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_quant_act(const void* x_bf16, int64_t rows, int64_t K, int32_t group,
+                  uint8_t* q, float* scale, void* stream) {
+  if (group != 0 && group != 128) return FP8DQ_ERR_FLAGS;
+  if (rows < 0 || K <= 0 || (K % (group ? 128 : 8)) != 0) return FP8DQ_ERR_SHAPE;
+  if (rows > INT32_MAX || K > INT32_MAX) return FP8DQ_ERR_SHAPE;
+  if (rows == 0) return FP8DQ_OK;
+  if (!x_bf16 || !q || !scale) return FP8DQ_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(q) || !aligned16(scale)) return FP8DQ_ERR_ALIGN;
+  if (group == 0)
+    fp8dq::launch_quant_rows(x_bf16, rows, K, q, scale, as_stream(stream));
+  else
+    fp8dq::launch_quant_groups(x_bf16, rows, K, q, scale, as_stream(stream));
+  return launch_status();
+}
+
+int fp8_quant_weight_block(const void* w_bf16, int64_t N, int64_t K, uint8_t* qw,
+                           float* sw, void* stream) {
+  if (N < 0 || K <= 0 || (N % 128) != 0 || (K % 128) != 0) return FP8DQ_ERR_SHAPE;
+  if (N > INT32_MAX || K > INT32_MAX) return FP8DQ_ERR_SHAPE;
+  if (N == 0) return FP8DQ_OK;
+  if (!w_bf16 || !qw || !sw) return FP8DQ_ERR_NULL;
+  if (!aligned16(w_bf16) || !aligned16(qw) || !aligned16(sw)) return FP8DQ_ERR_ALIGN;
+  fp8dq::launch_quant_wblock(w_bf16, N, K, qw, sw, as_stream(stream));
+  return launch_status();
+}
+
+int fp8_gemm(const uint8_t* qx, const float* sx, const uint8_t* qw,
+             const float* sw, void* y_bf16, int64_t M, int64_t N, int64_t K,
+             uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_gemm_args(qx, sx, qw, sw, y_bf16, M, N, K, flags, ws, ws_bytes, false);
+  if (s != FP8DQ_OK || M == 0 || N == 0) return s;
+  return run_gemm(qx, sx, qw, sw, y_bf16, M, N, K, flags, ws, false, as_stream(stream));
+}
+
+int fp8_gemm_block(const uint8_t* qx, const float* sx, const uint8_t* qw,
+                   const float* sw, void* y_bf16, int64_t M, int64_t N,
+                   int64_t K, uint32_t flags, void* ws, size_t ws_bytes,
+                   void* stream) {
+  int s = check_gemm_args(qx, sx, qw, sw, y_bf16, M, N, K, flags, ws, ws_bytes, true);
+  if (s != FP8DQ_OK || M == 0 || N == 0) return s;
+  return run_gemm(qx, sx, qw, sw, y_bf16, M, N, K, flags, ws, true, as_stream(stream));
+}
+
+static int linear_common(const void* x_bf16, const uint8_t* qw, const float* sw,
+                         void* y_bf16, int64_t M, int64_t N, int64_t K,
+                         uint8_t* qx_out, float* sx_out, uint32_t flags, void* ws,
+                         size_t ws_bytes, void* stream, bool block) {
+  int s = check_gemm_args(qx_out, sx_out, qw, sw, y_bf16, M, N, K, flags, ws,
+                          ws_bytes, block);
+  if (s != FP8DQ_OK || M == 0 || N == 0) return s;
+  if (!x_bf16) return FP8DQ_ERR_NULL;
+  if (!aligned16(x_bf16)) return FP8DQ_ERR_ALIGN;
+  hipStream_t st = as_stream(stream);
+  if (block) fp8dq::launch_quant_groups(x_bf16, M, K, qx_out, sx_out, st);
+  else fp8dq::launch_quant_rows(x_bf16, M, K, qx_out, sx_out, st);
+  s = launch_status();
+  if (s != FP8DQ_OK) return s;
+  return run_gemm(qx_out, sx_out, qw, sw, y_bf16, M, N, K, flags, ws, block, st);
+}
+
+int fp8_linear(const void* x_bf16, const uint8_t* qw, const float* sw,
+               void* y_bf16, int64_t M, int64_t N, int64_t K, uint8_t* qx_out,
+               float* sx_out, uint32_t flags, void* ws, size_t ws_bytes,
+               void* stream) {
+  return linear_common(x_bf16, qw, sw, y_bf16, M, N, K, qx_out, sx_out, flags,
+                       ws, ws_bytes, stream, false);
+}
+
+int fp8_linear_block(const void* x_bf16, const uint8_t* qw, const float* sw,
+                     void* y_bf16, int64_t M, int64_t N, int64_t K,
+                     uint8_t* qx_out, float* sx_out, uint32_t flags, void* ws,
+                     size_t ws_bytes, void* stream) {
+  return linear_common(x_bf16, qw, sw, y_bf16, M, N, K, qx_out, sx_out, flags,
+                       ws, ws_bytes, stream, true);
+}
+
+size_t fp8_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t block,
+                           uint32_t flags) {
+  if (!known_flags(flags)) return 0;
+  if (block && (N % 128) != 0) return 0;
+  return gemm_ws_bytes(M, N, K, flags);
+}
+
+const char* fp8_status_string(int status) {
+  switch (status) {
+    case FP8DQ_OK: return "ok";
+    case FP8DQ_ERR_NULL: return "null pointer";
+    case FP8DQ_ERR_SHAPE: return "bad shape";
+    case FP8DQ_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case FP8DQ_ERR_WORKSPACE: return "workspace too small";
+    case FP8DQ_ERR_FLAGS: return "unsupported flags or group";
+    case FP8DQ_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* fp8dq_version(void) { return "0.1.0"; }
+
+}  // extern "C"

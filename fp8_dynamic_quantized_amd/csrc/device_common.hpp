@@ -1,0 +1,71 @@
+// Device-side helpers shared by the FP8-Dynamic kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8dq {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte loads (plain and non-temporal) returning HIP's uint4.
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+constexpr float kE4M3Max = 448.0f;  // largest finite E4M3 magnitude
+
+// 16x16 output tile, K = 128 E4M3 x E4M3 products per MFMA, fp32 accumulate.
+// Operand layout (both A and B): lane l holds row (l % 16) of its operand
+// and 32 consecutive K-bytes of that row; the four lane groups l / 16 hold
+// the four 32-byte K slices. A and B use the same lane->K mapping, so any
+// consistent assignment of K bytes to (lane group, byte) gives the same sum.
+// Output: lane l holds C[4*(l/16) + r][l % 16], r = 0..3, where the first
+// index runs over A's rows and the second over B's rows.
+// Scale operands 0 select the unscaled instruction (plain E4M3 products).
+__device__ __forceinline__ v4f mfma_e4m3_16x16x128(const v8i& a, const v8i& b,
+                                                   const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0,
+                                                          0, 0);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Wave-wide (64 lanes) maximum of an unsigned value.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = __shfl_xor(v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+// Maximum over aligned groups of `width` lanes (width a power of two <= 64).
+template <int width>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = width / 2; off >= 1; off >>= 1) {
+    uint32_t o = __shfl_xor(v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+}  // namespace fp8dq

@@ -1,0 +1,40 @@
+// Host-side launchers of the gfx950 kernels. Arguments are validated by the
+// C-ABI layer (api.cpp) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8dq {
+
+// Dynamic quantization (quant.hip).
+void launch_quant_rows(const void* x, int64_t rows, int64_t K, uint8_t* q,
+                       float* scale, hipStream_t st);
+void launch_quant_groups(const void* x, int64_t rows, int64_t K, uint8_t* q,
+                         float* scale, hipStream_t st);
+void launch_quant_wblock(const void* w, int64_t N, int64_t K, uint8_t* q,
+                         float* scale, hipStream_t st);
+
+// Prefill GEMM (gemm_prefill.hip): LDS-tiled MFMA, fused epilogue.
+// block = false: per-channel scales sx[M], sw[N];
+// block = true : sx[M, K/128], sw[N/128, K/128].
+void launch_gemm_prefill(const uint8_t* qx, const float* sx, const uint8_t* qw,
+                         const float* sw, void* y, int64_t M, int64_t N,
+                         int64_t K, bool block, hipStream_t st);
+
+// Decode GEMM (gemm_decode.hip): small-M, HBM-streaming, split-K.
+struct DecodePlan {
+  int mb;            // 16-row blocks of M covered (M <= 16 * mb)
+  int nb;            // 16-row blocks of N per workgroup
+  int splits;        // K slices across the grid (1: no partials)
+  int kt_per_split;  // 128-wide K steps per slice
+};
+DecodePlan plan_decode(int64_t M, int64_t N, int64_t K);
+size_t decode_workspace_bytes(int64_t M, int64_t N, const DecodePlan& p);
+void launch_gemm_decode(const uint8_t* qx, const float* sx, const uint8_t* qw,
+                        const float* sw, void* y, float* ws, int64_t M,
+                        int64_t N, int64_t K, bool block, const DecodePlan& p,
+                        hipStream_t st);
+
+}  // namespace fp8dq

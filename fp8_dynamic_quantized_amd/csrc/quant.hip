@@ -1,0 +1,336 @@
+// Dynamic FP8 (E4M3) quantization kernels for gfx950.
+//
+// What is computed (Llama-3.1-8B-Instruct-FP8-Dynamic page, FP8 dynamic
+// quantization table; Llama-3.2-3B-Instruct-FP8-Block page, FP8 block
+// quantization table; E4M3 limits from the "Llama 3 精读实录" page, §2.1):
+//   per unit (a row, a 128-column group of a row, or a 128x128 block):
+//     amax = max |x|;  s = RN_fp32(amax / 448);  q = E4M3_RNE(x / s)
+// with the exact quotient x / s (s as stored), ties to the even code and the
+// sign of zero kept; an all-zero unit has s = 0 and codes +-0.
+//
+// Design (HBM-bound: 2 bytes in, 1 byte + scales out per element):
+//  * each lane owns 8-element (16-byte) chunks of the unit, loaded once and
+//    kept in registers between the amax pass and the quantize pass;
+//  * amax is an integer max over the bf16 bit patterns with the sign bit
+//    cleared (exact for finite inputs), reduced across the wave with lane
+//    shuffles and across waves through LDS;
+//  * the quotient is formed as y = x * RN(1/s) in fp32 and rounded by the
+//    hardware fp32->E4M3 conversion (round to nearest even). y is within
+//    2^-23 (relative) of x / s, so it can land on the wrong side of an E4M3
+//    rounding midpoint only when it is within a couple of fp32 ulps of one.
+//    Such lanes -- and lanes in the E4M3 subnormal range, where the midpoint
+//    test below does not apply -- take an exact fix-up: the sign of
+//    (midpoint * s - |x|) from one fused multiply-add decides the side (and
+//    exactly zero means a tie, resolved to the even code).
+//  * exact quotients never exceed 448.9 for bf16 inputs (the scale rounding
+//    moves them by at most a few parts per thousand, in the fp32-subnormal
+//    scale range), so y stays below 464, where the hardware conversion still
+//    rounds to 448; no clamp is needed.
+//  * scales below 2^-64 are handled by scaling x and s by 2^64 (exact), which
+//    keeps 1/s finite and the fix-up's product away from fp32 underflow.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace fp8dq {
+namespace {
+
+constexpr uint32_t kNearTol = 4;          // fp32 ulps of slack around a midpoint
+constexpr float kTinyScale = 0x1p-64f;    // scales below this are pre-scaled
+constexpr float kPreScale = 0x1p64f;
+
+// Exact E4M3 magnitude code of |x| / s given the fast candidate code.
+//   ax  : |x| (times the pre-scale p)    sp : s * p
+//   ay  : |y|, the fp32 estimate of |x| / s     c : candidate magnitude code
+__device__ __noinline__ uint32_t exact_code(float ax, float sp, float ay,
+                                            uint32_t c) {
+  float cv = __builtin_amdgcn_cvt_f32_fp8(c, 0);
+  if (ay == cv) return c;  // on a grid point: far from every midpoint
+  bool up = ay > cv;
+  if (up && c == 126u) return 126u;  // beyond 448: saturate
+  uint32_t c2 = up ? c + 1u : c - 1u;
+  float v2 = __builtin_amdgcn_cvt_f32_fp8(c2, 0);
+  float mid = 0.5f * (cv + v2);       // exact: at most five significant bits
+  float t = __builtin_fmaf(mid, sp, -ax);  // sign(mid*s - |x|), exact
+  uint32_t lo = up ? c : c2, hi = up ? c2 : c;
+  if (t > 0.0f) return lo;
+  if (t < 0.0f) return hi;
+  return (lo & 1u) ? hi : lo;  // exact tie: even code
+}
+
+// True when y needs the exact fix-up: its low 20 mantissa bits are within
+// kNearTol of the E4M3 normal-range midpoint pattern, or 0 < |y| < 2^-6.
+__device__ __forceinline__ bool needs_fixup(float y) {
+  uint32_t b = __float_as_uint(y);
+  bool near_mid = ((b + (kNearTol - 0x80000u)) << 12) <= ((2u * kNearTol) << 12);
+  bool small = ((b << 1) - 2u) < ((0x3C800000u << 1) - 2u);
+  return near_mid || small;
+}
+
+// Quantize 8 bf16 values (one 16-byte chunk) with scale s.
+// r = 1/(s*p) (0 when s == 0), p the pre-scale (1 or 2^64, PRE only).
+template <bool PRE>
+__device__ __forceinline__ uint2 quant8(uint4 raw, float s, float r, float p) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float x[8], y[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = (PRE ? x[i] * p : x[i]) * r;
+  uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+  uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+  const float sp = PRE ? s * p : s;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (needs_fixup(y[i])) {
+      uint32_t& word = (i < 4) ? lo : hi;
+      const int sh = 8 * (i & 3);
+      uint32_t cand = (word >> sh) & 0x7Fu;
+      float ax = __builtin_fabsf(PRE ? x[i] * p : x[i]);
+      uint32_t mag = exact_code(ax, sp, __builtin_fabsf(y[i]), cand);
+      uint32_t code = mag | ((__float_as_uint(x[i]) >> 24) & 0x80u);
+      word = (word & ~(0xFFu << sh)) | (code << sh);
+    }
+  }
+  return make_uint2(lo, hi);
+}
+
+// Largest |bf16| bit pattern (sign cleared) over a chunk, per 16-bit half.
+__device__ __forceinline__ us2 chunk_amax(uint4 v, us2 acc) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t a = w[i] & 0x7FFF7FFFu;
+    us2 h = __builtin_bit_cast(us2, a);
+    acc = __builtin_elementwise_max(acc, h);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ void unit_scale(uint32_t amax_bits, float& s,
+                                           float& r, float& p, bool& tiny) {
+  float amax = __uint_as_float(amax_bits << 16);
+  s = amax / kE4M3Max;  // IEEE division, correctly rounded
+  tiny = s < kTinyScale && s > 0.0f;
+  p = tiny ? kPreScale : 1.0f;
+  r = s > 0.0f ? 1.0f / (s * p) : 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Per-row quantization: one scale per row of [rows, K].
+// A team of TEAM_WAVES waves owns a row; each lane holds CH chunks of the row
+// in registers. Block = 256 threads (4 / TEAM_WAVES rows per block).
+// ---------------------------------------------------------------------------
+template <int CH, int TEAM_WAVES>
+__global__ __launch_bounds__(256) void quant_rows_kernel(
+    const uint4* __restrict__ x, int64_t rows, int64_t K, uint2* __restrict__ q,
+    float* __restrict__ scale) {
+  constexpr int TEAM = 64 * TEAM_WAVES;
+  constexpr int ROWS_PER_BLOCK = 4 / TEAM_WAVES;
+  __shared__ uint32_t red[4];
+  const int tid = threadIdx.x;
+  const int team = tid / TEAM;
+  const int tl = tid % TEAM;
+  const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + team;
+  const int64_t nch = K >> 3;  // chunks per row
+  const bool row_ok = row < rows;
+  const uint4* xr = x + (row_ok ? row : 0) * nch;
+
+  uint4 v[CH];
+  us2 m2 = {0, 0};
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int64_t c = (int64_t)i * TEAM + tl;
+    if (row_ok && c < nch) {
+      v[i] = ld16_nt(xr + c);
+    } else {
+      v[i] = make_uint4(0, 0, 0, 0);
+    }
+    m2 = chunk_amax(v[i], m2);
+  }
+  uint32_t m = m2.x > m2.y ? m2.x : m2.y;
+  m = wave_max_u32(m);
+  if (TEAM_WAVES > 1) {
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    m = red[0];
+#pragma unroll
+    for (int w = 1; w < TEAM_WAVES; ++w) m = m > red[w] ? m : red[w];
+  }
+  if (!row_ok) return;
+  float s, r, p;
+  bool tiny;
+  unit_scale(m, s, r, p, tiny);
+  if (tl == 0) scale[row] = s;
+  uint2* qr = q + row * nch;
+  if (!tiny) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int64_t c = (int64_t)i * TEAM + tl;
+      if (c < nch) qr[c] = quant8<false>(v[i], s, r, p);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int64_t c = (int64_t)i * TEAM + tl;
+      if (c < nch) qr[c] = quant8<true>(v[i], s, r, p);
+    }
+  }
+}
+
+// Rows longer than the register-resident kernels take (K > 32768): two
+// passes over the row, one block of 256 threads per row.
+__global__ __launch_bounds__(256) void quant_rows_2pass_kernel(
+    const uint4* __restrict__ x, int64_t rows, int64_t K, uint2* __restrict__ q,
+    float* __restrict__ scale) {
+  __shared__ uint32_t red[4];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int64_t nch = K >> 3;
+  const uint4* xr = x + row * nch;
+  us2 m2 = {0, 0};
+  for (int64_t c = tid; c < nch; c += 256) m2 = chunk_amax(xr[c], m2);
+  uint32_t m = m2.x > m2.y ? m2.x : m2.y;
+  m = wave_max_u32(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = red[0];
+  for (int w = 1; w < 4; ++w) m = m > red[w] ? m : red[w];
+  float s, r, p;
+  bool tiny;
+  unit_scale(m, s, r, p, tiny);
+  if (tid == 0) scale[row] = s;
+  uint2* qr = q + row * nch;
+  for (int64_t c = tid; c < nch; c += 256)
+    qr[c] = tiny ? quant8<true>(xr[c], s, r, p) : quant8<false>(xr[c], s, r, p);
+}
+
+// ---------------------------------------------------------------------------
+// Group-128 quantization (block variant's activations): 16 lanes per group,
+// one chunk each; each thread handles UNROLL chunks spaced by the block size.
+// ---------------------------------------------------------------------------
+template <int UNROLL>
+__global__ __launch_bounds__(256) void quant_groups_kernel(
+    const uint4* __restrict__ x, int64_t total_chunks, uint2* __restrict__ q,
+    float* __restrict__ scale) {
+  const int64_t base = (int64_t)blockIdx.x * 256 * UNROLL + threadIdx.x;
+  uint4 v[UNROLL];
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const int64_t c = base + (int64_t)u * 256;
+    v[u] = c < total_chunks ? ld16_nt(x + c) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const int64_t c = base + (int64_t)u * 256;
+    us2 m2 = chunk_amax(v[u], us2{0, 0});
+    uint32_t m = m2.x > m2.y ? m2.x : m2.y;
+    m = group_max_u32<16>(m);
+    float s, r, p;
+    bool tiny;
+    unit_scale(m, s, r, p, tiny);
+    if (c < total_chunks) {
+      if ((threadIdx.x & 15) == 0) scale[c >> 4] = s;
+    }
+    uint2 out;
+    if (__builtin_expect(__any(tiny), 0)) {
+      out = quant8<true>(v[u], s, r, p);
+    } else {
+      out = quant8<false>(v[u], s, r, p);
+    }
+    if (c < total_chunks) q[c] = out;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 block weight quantization: one 256-thread block per weight block.
+// Thread t covers rows (t / 16) + 16 i, i = 0..7, chunk t % 16 of the block.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_wblock_kernel(
+    const uint4* __restrict__ w, int64_t N, int64_t K, uint2* __restrict__ q,
+    float* __restrict__ scale) {
+  __shared__ uint32_t red[4];
+  const int tid = threadIdx.x;
+  const int64_t kb = blockIdx.x, nb = blockIdx.y;
+  const int64_t nch = K >> 3;
+  const int64_t col = kb * 16 + (tid & 15);
+  uint4 v[8];
+  us2 m2 = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = nb * 128 + (tid >> 4) + 16 * i;
+    v[i] = w[r * nch + col];
+    m2 = chunk_amax(v[i], m2);
+  }
+  uint32_t m = m2.x > m2.y ? m2.x : m2.y;
+  m = wave_max_u32(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = red[0];
+  for (int i = 1; i < 4; ++i) m = m > red[i] ? m : red[i];
+  float s, r, p;
+  bool tiny;
+  unit_scale(m, s, r, p, tiny);
+  if (tid == 0) scale[nb * (K >> 7) + kb] = s;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t rr = nb * 128 + (tid >> 4) + 16 * i;
+    q[rr * nch + col] = tiny ? quant8<true>(v[i], s, r, p)
+                             : quant8<false>(v[i], s, r, p);
+  }
+}
+
+template <int CH, int TW>
+void launch_rows(const void* x, int64_t rows, int64_t K, uint8_t* q,
+                 float* scale, hipStream_t st) {
+  constexpr int RPB = 4 / TW;
+  const int64_t blocks = (rows + RPB - 1) / RPB;
+  hipLaunchKernelGGL((quant_rows_kernel<CH, TW>), dim3((unsigned)blocks),
+                     dim3(256), 0, st, (const uint4*)x, rows, K, (uint2*)q,
+                     scale);
+}
+
+}  // namespace
+
+// Host launchers (validated arguments only).
+void launch_quant_rows(const void* x, int64_t rows, int64_t K, uint8_t* q,
+                       float* scale, hipStream_t st) {
+  const int64_t nch = K / 8;
+  // One wave per row while the row fits 16 chunks per lane, else 4 waves.
+  if (nch <= 64 * 1) launch_rows<1, 1>(x, rows, K, q, scale, st);
+  else if (nch <= 64 * 2) launch_rows<2, 1>(x, rows, K, q, scale, st);
+  else if (nch <= 64 * 4) launch_rows<4, 1>(x, rows, K, q, scale, st);
+  else if (nch <= 64 * 6) launch_rows<6, 1>(x, rows, K, q, scale, st);
+  else if (nch <= 64 * 8) launch_rows<8, 1>(x, rows, K, q, scale, st);
+  else if (nch <= 256 * 3) launch_rows<3, 4>(x, rows, K, q, scale, st);
+  else if (nch <= 256 * 4) launch_rows<4, 4>(x, rows, K, q, scale, st);
+  else if (nch <= 256 * 6) launch_rows<6, 4>(x, rows, K, q, scale, st);
+  else if (nch <= 256 * 8) launch_rows<8, 4>(x, rows, K, q, scale, st);
+  else if (nch <= 256 * 12) launch_rows<12, 4>(x, rows, K, q, scale, st);
+  else if (nch <= 256 * 16) launch_rows<16, 4>(x, rows, K, q, scale, st);
+  else
+    hipLaunchKernelGGL(quant_rows_2pass_kernel, dim3((unsigned)rows), dim3(256),
+                       0, st, (const uint4*)x, rows, K, (uint2*)q, scale);
+}
+
+void launch_quant_groups(const void* x, int64_t rows, int64_t K, uint8_t* q,
+                         float* scale, hipStream_t st) {
+  constexpr int U = 4;
+  const int64_t total = rows * (K / 8);
+  const int64_t blocks = (total + 256 * U - 1) / (256 * U);
+  hipLaunchKernelGGL((quant_groups_kernel<U>), dim3((unsigned)blocks),
+                     dim3(256), 0, st, (const uint4*)x, total, (uint2*)q,
+                     scale);
+}
+
+void launch_quant_wblock(const void* w, int64_t N, int64_t K, uint8_t* q,
+                         float* scale, hipStream_t st) {
+  hipLaunchKernelGGL(quant_wblock_kernel, dim3((unsigned)(K / 128), (unsigned)(N / 128)),
+                     dim3(256), 0, st, (const uint4*)w, N, K, (uint2*)q, scale);
+}
+
+}  // namespace fp8dq

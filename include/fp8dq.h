@@ -1,0 +1,175 @@
+/*
+ * fp8dq.h -- FP8-Dynamic quantized linear layer for AMD MI355X (gfx950).
+ *
+ * The operation (as the pages define it):
+ *   - Activations are quantized at run time, one scale per token (row of X),
+ *     to FP8 E4M3 -- Llama-3.1-8B-Instruct-FP8-Dynamic page, FP8 dynamic
+ *     quantization table (input activations row); Llama-3.1-70B-FP8-Dynamic
+ *     page, section 1.2 (activations bullet).
+ *   - Weights are stored as E4M3 with one scale per output channel (row of
+ *     W), found with a min/max observer -- same table, weights row; 70B page,
+ *     section 1.2, weights bullet; one weight_scale beside every Linear (70B
+ *     page, section 2).
+ *   - Block variant: one weight scale per 128x128 block of W, activation
+ *     scales per token per 128-column group, both dynamic for activations --
+ *     Llama-3.2-3B-Instruct-FP8-Block page, FP8 block quantization table.
+ *   - E4M3 is the 4-exponent/3-mantissa-bit format whose largest value is
+ *     448 -- "Llama 3 精读实录" page, section 2.1.
+ *   - lm_head is never quantized (ignore list on all three walk-through
+ *     pages): nothing in this library applies to it; callers keep it bf16.
+ *
+ * Numerics (fixed here where the pages are silent):
+ *   amax  = max |x| over the unit (row, 128-group, W row or 128x128 block)
+ *   s     = RN_fp32(amax / 448), stored as fp32; s = 0 for an all-zero unit
+ *   q     = E4M3 code nearest to the exact quotient x / s (ties to the even
+ *           code, saturating at +-448, sign of zero kept); q = +-0 if s = 0
+ *   y     = bf16_RNE( sum_k val(qx[m,k]) val(qw[n,k]) * sx[m] * sw[n] )
+ *   block: y = bf16_RNE( sum_g (sum_{k in g} val*val) * sx[m,g] * sw[n/128,g] )
+ *   The sum is accumulated in fp32 (any order); codes and scales are
+ *   bit-exact, y is within 1e-2 relative / 1e-3 absolute of the exact value.
+ *
+ * Conventions for every entry point:
+ *   - extern "C"; no C++ exception crosses the boundary.
+ *   - All tensor pointers are caller-owned DEVICE memory, row-major and
+ *     contiguous, 16-byte aligned. X is bf16 [M,K], W is bf16 [N,K] (K is
+ *     the contiguous dimension of both), Y is bf16 [M,N]; codes are uint8
+ *     E4M3 with the same shapes; scales are fp32.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously on it; nothing synchronizes.
+ *   - All arguments are validated on the host before anything is enqueued;
+ *     on any error nothing is enqueued and outputs are untouched.
+ *   - The library allocates and frees nothing, keeps no pointer after it
+ *     returns and holds no mutable global state: calls are reentrant.
+ *     Concurrent calls that write the same buffers race (caller's problem).
+ *   - Inputs and outputs must not overlap. Inputs must be finite (NaN / Inf
+ *     are outside the contract: not checked, result unspecified).
+ *   - M = 0 or N = 0 (rows = 0) is a valid empty call: FP8DQ_OK, nothing
+ *     enqueued. Negative sizes are FP8DQ_ERR_SHAPE.
+ */
+#ifndef FP8DQ_H
+#define FP8DQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define FP8DQ_OK              0
+#define FP8DQ_ERR_NULL       -1  /* a required pointer is NULL */
+#define FP8DQ_ERR_SHAPE      -2  /* negative size, or a size rule below broken */
+#define FP8DQ_ERR_ALIGN      -3  /* a tensor pointer is not 16-byte aligned */
+#define FP8DQ_ERR_WORKSPACE  -4  /* workspace smaller than fp8_workspace_bytes() */
+#define FP8DQ_ERR_FLAGS      -5  /* unknown flag bits or group value */
+#define FP8DQ_ERR_HIP        -6  /* the HIP runtime reported a launch error */
+
+/* flags for the GEMM / linear calls: which kernel family runs. */
+#define FP8DQ_AUTO            0u  /* M <= 64: split-K decode path, else prefill */
+#define FP8DQ_FORCE_PREFILL   1u  /* LDS-tiled MFMA GEMM at any M */
+#define FP8DQ_FORCE_DECODE    2u  /* HBM-streaming split-K GEMM at any M */
+
+/* Largest M the decode (small-M) path takes under FP8DQ_AUTO. */
+#define FP8DQ_DECODE_MAX_M   64
+
+/*
+ * fp8_quant_act -- dynamic activation quantization (also the per-channel
+ * weight quantizer: rows of W are output channels, same arithmetic).
+ *   x      : bf16 [rows, K]
+ *   group  : 0   -> one scale per row,           scale is fp32 [rows]
+ *            128 -> one scale per row per 128 columns, scale is fp32
+ *                   [rows, K/128] (block variant's activations)
+ *   q      : uint8 E4M3 codes [rows, K] (output)
+ *   scale  : fp32 scales (output), layout as above
+ * Size rules: rows >= 0; K > 0 and K % 8 == 0 (group 0) or K % 128 == 0
+ * (group 128). Any other group value is FP8DQ_ERR_FLAGS.
+ * Source: FP8 dynamic quantization table (input activations / weights rows)
+ * on the Llama-3.1-8B-Instruct-FP8-Dynamic page; block table on the
+ * Llama-3.2-3B-Instruct-FP8-Block page (group 128).
+ */
+int fp8_quant_act(const void* x_bf16, int64_t rows, int64_t K, int32_t group,
+                  uint8_t* q, float* scale, void* stream);
+
+/*
+ * fp8_quant_weight_block -- 128x128 block weight quantization (setup step
+ * of the block variant).
+ *   w  : bf16 [N, K];  qw : uint8 [N, K] (output);
+ *   sw : fp32 [N/128, K/128] (output), block (nb, kb) covers rows
+ *        128nb..128nb+127 and columns 128kb..128kb+127.
+ * Size rules: N >= 0, K > 0, N % 128 == 0, K % 128 == 0.
+ * Source: block_structure [128, 128] in the FP8 block quantization table,
+ * Llama-3.2-3B-Instruct-FP8-Block page.
+ */
+int fp8_quant_weight_block(const void* w_bf16, int64_t N, int64_t K,
+                           uint8_t* qw, float* sw, void* stream);
+
+/*
+ * fp8_gemm -- Y = bf16( (Qx Qw^T) * sx[m] * sw[n] ) from codes and scales.
+ *   qx : uint8 [M, K], sx : fp32 [M];  qw : uint8 [N, K], sw : fp32 [N]
+ *   y  : bf16 [M, N] (output)
+ *   flags : FP8DQ_AUTO / FP8DQ_FORCE_PREFILL / FP8DQ_FORCE_DECODE
+ *   ws, ws_bytes : device workspace for split-K partial sums; ws may be
+ *        NULL iff fp8_workspace_bytes(M, N, K, 0, flags) == 0.
+ * Size rules: M, N >= 0; K > 0 and K % 128 == 0.
+ */
+int fp8_gemm(const uint8_t* qx, const float* sx, const uint8_t* qw,
+             const float* sw, void* y_bf16, int64_t M, int64_t N, int64_t K,
+             uint32_t flags, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * fp8_gemm_block -- block-scaled GEMM:
+ *   y[m,n] = bf16( sum_g P_g[m,n] * sx[m,g] * sw[n/128, g] ), P_g the code
+ *   product summed over the g-th 128-column group.
+ *   sx : fp32 [M, K/128];  sw : fp32 [N/128, K/128]
+ * Size rules: M, N >= 0; N % 128 == 0; K > 0 and K % 128 == 0.
+ * ws as for fp8_gemm (block = 1 in fp8_workspace_bytes).
+ */
+int fp8_gemm_block(const uint8_t* qx, const float* sx, const uint8_t* qw,
+                   const float* sw, void* y_bf16, int64_t M, int64_t N,
+                   int64_t K, uint32_t flags, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/*
+ * fp8_linear -- the FP8-Dynamic linear: quantize X per token (writes qx_out,
+ * sx_out, which the caller owns and may inspect) and run fp8_gemm with the
+ * pre-quantized weight (qw, sw from fp8_quant_act on W).
+ *   x : bf16 [M, K]; qx_out : uint8 [M, K]; sx_out : fp32 [M]
+ * Size rules: those of fp8_gemm.
+ */
+int fp8_linear(const void* x_bf16, const uint8_t* qw, const float* sw,
+               void* y_bf16, int64_t M, int64_t N, int64_t K,
+               uint8_t* qx_out, float* sx_out, uint32_t flags, void* ws,
+               size_t ws_bytes, void* stream);
+
+/*
+ * fp8_linear_block -- block variant: quantize X per token per 128-group
+ * (qx_out uint8 [M, K], sx_out fp32 [M, K/128]) then fp8_gemm_block with
+ * block-quantized weights (qw, sw from fp8_quant_weight_block).
+ * Size rules: those of fp8_gemm_block.
+ */
+int fp8_linear_block(const void* x_bf16, const uint8_t* qw, const float* sw,
+                     void* y_bf16, int64_t M, int64_t N, int64_t K,
+                     uint8_t* qx_out, float* sx_out, uint32_t flags, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/*
+ * fp8_workspace_bytes -- device workspace the GEMM / linear calls need for
+ * these sizes and flags (block = 0: per-channel, 1: block variant). 0 when
+ * the chosen path needs none. Pure host function; never fails (returns 0 for
+ * invalid sizes, which the compute calls then reject).
+ */
+size_t fp8_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t block,
+                           uint32_t flags);
+
+/* fp8_status_string -- static text for a status code (never NULL). */
+const char* fp8_status_string(int status);
+
+/* fp8dq_version -- library version string, "major.minor.patch". */
+const char* fp8dq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8DQ_H */

@@ -1,0 +1,115 @@
+"""The C-ABI library loads, exports what include/fp8dq.h declares and rejects
+bad arguments on the host (no GPU needed: every case below returns before
+anything would be enqueued)."""
+import ctypes
+import os
+
+import pytest
+
+import fp8_dynamic_quantized_amd as F
+from fp8_dynamic_quantized_amd import build as B
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB):
+        B.build()
+    return F.lib()
+
+
+P = ctypes.c_void_p
+A = P(0x10000)          # a 16-byte aligned stand-in address (never dereferenced)
+MIS = P(0x10004)        # misaligned stand-in
+
+
+def test_exports_every_declared_symbol(L):
+    names = F.header_functions()
+    assert {"fp8_quant_act", "fp8_linear", "fp8_linear_block"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert F.fp8_status_string(code) not in ("", "unknown status")
+    assert F.fp8_status_string(99) == "unknown status"
+    assert F.fp8dq_version().count(".") == 2
+
+
+def test_quant_act_errors(L):
+    q = L.fp8_quant_act
+    assert q(None, 4, 64, 0, A, A, None) == -1
+    assert q(A, 4, 64, 0, None, A, None) == -1
+    assert q(A, 4, 64, 0, A, None, None) == -1
+    assert q(A, -1, 64, 0, A, A, None) == -2
+    assert q(A, 4, 0, 0, A, A, None) == -2
+    assert q(A, 4, 60, 0, A, A, None) == -2        # K % 8
+    assert q(A, 4, 192, 128, A, A, None) == -2     # K % 128 for groups
+    assert q(A, 4, 64, 64, A, A, None) == -5       # group must be 0 or 128
+    assert q(MIS, 4, 64, 0, A, A, None) == -3
+    assert q(A, 4, 64, 0, MIS, A, None) == -3
+    assert q(None, 0, 64, 0, None, None, None) == 0  # empty: nothing to do
+
+
+def test_quant_weight_block_errors(L):
+    f = L.fp8_quant_weight_block
+    assert f(None, 128, 128, A, A, None) == -1
+    assert f(A, 100, 128, A, A, None) == -2
+    assert f(A, 128, 100, A, A, None) == -2
+    assert f(A, 128, 128, MIS, A, None) == -3
+    assert f(None, 0, 128, None, None, None) == 0
+
+
+@pytest.mark.parametrize("fn", ["fp8_gemm", "fp8_gemm_block"])
+def test_gemm_errors(L, fn):
+    g = getattr(L, fn)
+    assert g(None, A, A, A, A, 16, 128, 128, 0, None, 0, None) == -1
+    assert g(A, A, A, A, None, 16, 128, 128, 0, None, 0, None) == -1
+    assert g(A, A, A, A, A, -1, 128, 128, 0, None, 0, None) == -2
+    assert g(A, A, A, A, A, 16, 128, 100, 0, None, 0, None) == -2   # K % 128
+    assert g(A, A, A, A, A, 16, 128, 0, 0, None, 0, None) == -2
+    assert g(A, A, A, A, A, 16, 128, 128, 7, None, 0, None) == -5
+    assert g(A, A, MIS, A, A, 100, 128, 128, 1, None, 0, None) == -3
+    assert g(A, A, A, A, A, 0, 128, 128, 0, None, 0, None) == 0     # empty M
+    assert g(None, None, None, None, None, 16, 0, 128, 0, None, 0, None) == 0
+
+
+def test_gemm_block_needs_n_multiple_of_128(L):
+    assert L.fp8_gemm_block(A, A, A, A, A, 16, 200, 128, 0, None, 0, None) == -2
+    assert L.fp8_linear_block(A, A, A, A, 16, 200, 128, A, A, 0, None, 0, None) == -2
+
+
+def test_workspace_rules(L):
+    # a small-N decode shape splits K and needs a workspace; prefill needs none
+    need = F.fp8_workspace_bytes(16, 1024, 4096)
+    assert need > 0 and need % 4 == 0
+    assert F.fp8_workspace_bytes(4096, 4096, 4096) == 0
+    assert F.fp8_workspace_bytes(16, 1024, 4096, flags=F.FORCE_PREFILL) == 0
+    assert F.fp8_workspace_bytes(16, 1024, 100) == 0       # invalid K -> 0
+    assert F.fp8_workspace_bytes(16, 1000, 4096, block=True) == 0  # invalid N
+    g = L.fp8_gemm
+    assert g(A, A, A, A, A, 16, 1024, 4096, 0, None, 0, None) == -1
+    assert g(A, A, A, A, A, 16, 1024, 4096, 0, A, need - 4, None) == -4
+    assert g(A, A, A, A, A, 16, 1024, 4096, 0, MIS, need, None) == -3
+    # M beyond one decode slab uses the slab's workspace size
+    assert F.fp8_workspace_bytes(200, 1024, 4096, flags=F.FORCE_DECODE) == \
+        F.fp8_workspace_bytes(64, 1024, 4096)
+
+
+@pytest.mark.parametrize("fn", ["fp8_linear", "fp8_linear_block"])
+def test_linear_errors(L, fn):
+    f = getattr(L, fn)
+    assert f(None, A, A, A, 16, 128, 128, A, A, 0, None, 0, None) == -1
+    assert f(A, A, A, A, 16, 128, 128, None, A, 0, None, 0, None) == -1
+    assert f(MIS, A, A, A, 16, 128, 128, A, A, 0, None, 0, None) == -3
+    assert f(A, A, A, A, 16, 128, 96, A, A, 0, None, 0, None) == -2
+    assert f(A, A, A, A, 16, 128, 128, A, A, 9, None, 0, None) == -5
+    assert f(None, None, None, None, 0, 128, 128, None, None, 0, None, 0, None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from fp8_dynamic_quantized_amd import _binding
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _binding.lib()

@@ -1,0 +1,395 @@
+"""GPU parity: the HIP library (through the C-ABI) against the CPU oracle.
+
+Codes and scales must match bit for bit; bf16 outputs must be within
+1e-2 relative / 1e-3 absolute of the oracle's float64 value. Inputs are the
+seeded synthetic workloads of `synth` (same bytes on both sides). At full
+sizes the oracle computes sampled rows / columns; every expected value comes
+from the oracle alone.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.fp8dq_oracle as O
+import synth
+from gpu_util import (assert_codes_equal, assert_scales_equal, assert_y_close,
+                      dev, dev_bf16, ensure_built, host_bf16_f64, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def F():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return ensure_built()
+
+
+def sample_idx(n, k, seed):
+    rng = np.random.default_rng(seed)
+    edge = min(16, n)
+    idx = np.concatenate([np.arange(edge), np.arange(n - edge, n),
+                          rng.choice(n, size=min(k, n), replace=False)])
+    return np.unique(idx)
+
+
+# ----------------------------------------------------------------------------
+# Quantizers
+# ----------------------------------------------------------------------------
+ROW_SHAPES = [(1, 8), (3, 40), (5, 512), (7, 520), (64, 4096), (33, 3072),
+              (17, 8192), (9, 14336), (5, 28672), (3, 40960), (2, 65536),
+              (130, 1024)]
+
+
+@pytest.mark.parametrize("rows,K", ROW_SHAPES)
+def test_quant_rows(F, rows, K):
+    say(f"quant rows {rows}x{K}")
+    xb = synth.activations(rows, K, 100 + K, 200 + K)
+    if rows > 2:
+        xb[1] = 0                                          # all-zero row
+        xb[2, :] = 0x8000                                  # all -0.0 row
+    q, s = F.fp8_quant_act(dev_bf16(xb))
+    torch.cuda.synchronize()
+    q_o, s_o = O.quant_per_row(xb)
+    assert_scales_equal(s.cpu().numpy(), s_o, "scales")
+    assert_codes_equal(q.cpu().numpy(), q_o, "codes")
+
+
+def _near_tie_rows(amax_bits: np.ndarray, width: int, seed: int) -> np.ndarray:
+    """Rows whose amax is each given bf16 value; the rest are values close to
+    E4M3 rounding midpoints of x / s, plus random values below amax."""
+    rng = np.random.default_rng(seed)
+    R = len(amax_bits)
+    amax = O.bf16_to_f64(amax_bits)
+    s = O.scale_from_amax(amax).astype(np.float64)
+    grid = O.E4M3_VALUES[:127]
+    mids = (grid[:-1] + grid[1:]) / 2
+    half = width // 2
+    pick = mids[rng.integers(0, 125, size=(R, half))]          # below 440
+    near = synth.f32_to_bf16_bits((pick * s[:, None]).astype(np.float32)).astype(np.int32)
+    near = near + rng.integers(-1, 2, size=(R, half))           # +-1 ulp nudges
+    rnd = rng.uniform(0, 1, size=(R, width - half)) * amax[:, None]
+    far = synth.f32_to_bf16_bits(rnd.astype(np.float32)).astype(np.int32)
+    mag = np.concatenate([near, far], axis=1)
+    mag = np.clip(mag, 0, amax_bits.astype(np.int32)[:, None])  # |x| <= amax
+    sign = rng.integers(0, 2, size=(R, width)).astype(np.int32) << 15
+    x = (mag | sign).astype(np.uint16)
+    x[:, 0] = amax_bits | (np.uint16(0x8000) * (rng.integers(0, 2, R) == 1)).astype(np.uint16)
+    return x
+
+
+@pytest.mark.parametrize("group", [0, 128])
+def test_quant_every_bf16_amax_near_ties(F, group):
+    """Every positive finite bf16 amax (incl. fp32-subnormal scales and the
+    2^-64 pre-scale range), rows dense in near-midpoint quotients."""
+    say(f"quant exhaustive amax, group={group}")
+    amax_bits = np.arange(1, 0x7F80, dtype=np.uint16)
+    xb = _near_tie_rows(amax_bits, 128, seed=17 + group)
+    q, s = F.fp8_quant_act(dev_bf16(xb), group=group)
+    torch.cuda.synchronize()
+    q_o, s_o = O.quant_per_row(xb)
+    s_h = s.cpu().numpy().reshape(-1)
+    assert_scales_equal(s_h, s_o, "scales")
+    assert_codes_equal(q.cpu().numpy(), q_o, "codes")
+
+
+@pytest.mark.parametrize("rows,K", [(1, 128), (5, 384), (64, 3072), (17, 8192), (300, 256)])
+def test_quant_groups(F, rows, K):
+    say(f"quant groups {rows}x{K}")
+    xb = synth.activations(rows, K, 300 + K, 400 + K)
+    if rows > 2:
+        xb[1, 128:256] = 0                                 # one all-zero group
+    q, s = F.fp8_quant_act(dev_bf16(xb), group=128)
+    torch.cuda.synchronize()
+    q_o, s_o = O.quant_per_group(xb)
+    assert_scales_equal(s.cpu().numpy(), s_o, "group scales")
+    assert_codes_equal(q.cpu().numpy(), q_o, "group codes")
+
+
+@pytest.mark.parametrize("N,K", [(128, 128), (256, 384), (1024, 3072)])
+def test_quant_weight_block(F, N, K):
+    say(f"quant weight block {N}x{K}")
+    wb = synth.weights(N, K, 500 + N + K)
+    wb[0:128, 0:128] = 0                                   # an all-zero block
+    q, s = F.fp8_quant_weight_block(dev_bf16(wb))
+    torch.cuda.synchronize()
+    q_o, s_o = O.quant_weight_block(wb)
+    assert_scales_equal(s.cpu().numpy(), s_o, "block scales")
+    assert_codes_equal(q.cpu().numpy(), q_o, "block codes")
+
+
+# ----------------------------------------------------------------------------
+# GEMM core
+# ----------------------------------------------------------------------------
+FINITE = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+
+
+@pytest.mark.parametrize("flags", [1, 2])
+def test_mfma_product_table(F, flags):
+    """Every product of two finite E4M3 values is exact in bf16: with unit
+    scales and one nonzero code per row the output is the exact table."""
+    say(f"product table flags={flags}")
+    K = 256
+    qa = np.zeros((254, K), np.uint8)
+    for r, c in enumerate(FINITE):
+        qa[r, (r * 37) % K] = c
+        qa[r, 200] = c                       # shared position: products land here
+    qa_dev = dev(qa)
+    ones = dev(np.ones(254, np.float32))
+    y = F.fp8_gemm(qa_dev, ones, qa_dev, ones, flags=flags)
+    torch.cuda.synchronize()
+    want = O.linear_per_channel(qa, np.ones(254, np.float32), qa, np.ones(254, np.float32))
+    got = host_bf16_f64(y)
+    assert np.array_equal(O.f64_to_bf16_rne(want), want)     # exact in bf16
+    diff = got != want
+    assert not diff.any(), f"{diff.sum()} mismatches, first {np.argwhere(diff)[0]}"
+
+
+GEMM_SHAPES = [(1, 16, 128), (16, 1024, 4096), (65, 130, 256), (300, 200, 384),
+               (513, 1030, 1024), (256, 256, 128), (1000, 1000, 512), (64, 8192, 1024),
+               (2048, 512, 640)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+@pytest.mark.parametrize("flags", [0, 1, 2])
+def test_gemm_parity(F, M, N, K, flags):
+    say(f"gemm {M}x{N}x{K} flags={flags}")
+    xb = synth.activations(M, K, 600 + M, 700 + K)
+    wb = synth.weights(N, K, 800 + N + K)
+    qx, sx = O.quant_per_row(xb)
+    qw, sw = O.quant_per_row(wb)
+    y = F.fp8_gemm(dev(qx), dev(sx), dev(qw), dev(sw), flags=flags)
+    torch.cuda.synchronize()
+    assert_y_close(host_bf16_f64(y), O.linear_per_channel(qx, sx, qw, sw), "y")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (16, 1024, 3072), (65, 256, 384),
+                                   (300, 384, 1024), (1000, 640, 512)])
+@pytest.mark.parametrize("flags", [0, 1, 2])
+def test_gemm_block_parity(F, M, N, K, flags):
+    say(f"gemm block {M}x{N}x{K} flags={flags}")
+    xb = synth.activations(M, K, 900 + M, 1000 + K)
+    wb = synth.weights(N, K, 1100 + N + K)
+    qx, sx = O.quant_per_group(xb)
+    qw, sw = O.quant_weight_block(wb)
+    y = F.fp8_gemm_block(dev(qx), dev(sx), dev(qw), dev(sw), flags=flags)
+    torch.cuda.synchronize()
+    assert_y_close(host_bf16_f64(y), O.linear_block(qx, sx, qw, sw), "y")
+
+
+def test_gemm_random_codes_small_k(F):
+    """Uniformly random finite codes and scales (not only synthetic data)."""
+    rng = np.random.default_rng(5)
+    for (M, N, K, flags) in [(40, 48, 128, 0), (100, 64, 128, 1), (7, 33, 128, 2)]:
+        qx = rng.choice(FINITE, size=(M, K))
+        qw = rng.choice(FINITE, size=(N, K))
+        sx = rng.uniform(1e-4, 1e-3, M).astype(np.float32)
+        sw = rng.uniform(1e-4, 1e-3, N).astype(np.float32)
+        y = F.fp8_gemm(dev(qx), dev(sx), dev(qw), dev(sw), flags=flags)
+        torch.cuda.synchronize()
+        assert_y_close(host_bf16_f64(y), O.linear_per_channel(qx, sx, qw, sw),
+                       f"random codes {M}x{N}x{K} flags={flags}")
+
+
+# ----------------------------------------------------------------------------
+# The whole linear on the workloads
+# ----------------------------------------------------------------------------
+def _linear_case(F, xb, wb, cols, flags=0, what=""):
+    """GPU: W per-channel quantization + fp8_linear. Oracle: sampled W rows
+    (output columns `cols`), all X rows."""
+    x_d = dev_bf16(xb)
+    w_d = dev_bf16(wb)
+    qw_d, sw_d = F.fp8_quant_act(w_d)
+    y_d, qx_d, sx_d = F.fp8_linear(x_d, qw_d, sw_d, flags=flags)
+    torch.cuda.synchronize()
+    qw_o, sw_o = O.quant_per_row(wb[cols])
+    assert_scales_equal(sw_d.cpu().numpy()[cols], sw_o, f"{what} weight scales")
+    assert_codes_equal(qw_d.cpu().numpy()[cols], qw_o, f"{what} weight codes")
+    qx_o, sx_o = O.quant_per_row(xb)
+    assert_scales_equal(sx_d.cpu().numpy(), sx_o, f"{what} act scales")
+    assert_codes_equal(qx_d.cpu().numpy(), qx_o, f"{what} act codes")
+    y_ref = O.linear_per_channel(qx_o, sx_o, qw_o, sw_o)
+    assert_y_close(host_bf16_f64(y_d[:, torch.from_numpy(cols).cuda()]), y_ref, f"{what} y")
+
+
+def test_c1_single_linear(F):
+    d = synth.workload(1)
+    say("c1 16x4096->1024")
+    _linear_case(F, d["x"], d["w"], np.arange(d["N"]), what="c1")
+
+
+@pytest.mark.parametrize("j", [0, 1, 2, 3])
+@pytest.mark.parametrize("M", [64, 256])
+def test_c2_prefill_shapes(F, j, M):
+    d = synth.workload(2, j, M=M)
+    say(f"c2 {d['name']} M={M} K={d['K']} N={d['N']}")
+    _linear_case(F, d["x"], d["w"], sample_idx(d["N"], 256, j), what=f"c2 {d['name']}")
+
+
+@pytest.mark.parametrize("j", [0, 1, 2, 3])
+def test_c3_decode_shapes(F, j):
+    name, K, N = synth.SHAPES["c3"][j]
+    say(f"c3 {name} K={K} N={N}: weights")
+    wb = synth.weights(N, K, synth.seed_of(3, j, 0, 1))
+    w_d = dev_bf16(wb)
+    qw_d, sw_d = F.fp8_quant_act(w_d)
+    del w_d
+    cols = sample_idx(N, 192, 10 + j)
+    qw_o, sw_o = O.quant_per_row(wb[cols])
+    del wb
+    torch.cuda.synchronize()
+    assert_scales_equal(sw_d.cpu().numpy()[cols], sw_o, "weight scales")
+    assert_codes_equal(qw_d.cpu().numpy()[cols], qw_o, "weight codes")
+    cols_d = torch.from_numpy(cols).cuda()
+    for i, M in enumerate(synth.M_OF["c3"]):
+        say(f"c3 {name} M={M}")
+        xb = synth.workload(3, j, i, w=False)["x"]
+        y_d, qx_d, sx_d = F.fp8_linear(dev_bf16(xb), qw_d, sw_d)
+        torch.cuda.synchronize()
+        qx_o, sx_o = O.quant_per_row(xb)
+        assert_scales_equal(sx_d.cpu().numpy(), sx_o, "act scales")
+        assert_codes_equal(qx_d.cpu().numpy(), qx_o, "act codes")
+        assert_y_close(host_bf16_f64(y_d[:, cols_d]),
+                       O.linear_per_channel(qx_o, sx_o, qw_o, sw_o), f"M={M} y")
+
+
+@pytest.mark.parametrize("j", [0, 1, 2, 3])
+@pytest.mark.parametrize("M", [64, 512])
+def test_c4_block_shapes(F, j, M):
+    d = synth.workload(4, j, M=M)
+    N, K = d["N"], d["K"]
+    say(f"c4 {d['name']} M={M} K={K} N={N}")
+    x_d = dev_bf16(d["x"])
+    w_d = dev_bf16(d["w"])
+    qw_d, sw_d = F.fp8_quant_weight_block(w_d)
+    y_d, qx_d, sx_d = F.fp8_linear_block(x_d, qw_d, sw_d)
+    torch.cuda.synchronize()
+    bands = np.unique([0, N // 128 - 1, (N // 128) // 2])
+    rows = np.concatenate([np.arange(b * 128, b * 128 + 128) for b in bands])
+    qw_o, sw_o = O.quant_weight_block(d["w"][rows])
+    assert_scales_equal(sw_d.cpu().numpy()[bands], sw_o, "block weight scales")
+    assert_codes_equal(qw_d.cpu().numpy()[rows], qw_o, "block weight codes")
+    qx_o, sx_o = O.quant_per_group(d["x"])
+    assert_scales_equal(sx_d.cpu().numpy(), sx_o, "group act scales")
+    assert_codes_equal(qx_d.cpu().numpy(), qx_o, "group act codes")
+    y_ref = O.linear_block(qx_o, sx_o, qw_o, sw_o)
+    assert_y_close(host_bf16_f64(y_d[:, torch.from_numpy(rows).cuda()]), y_ref, "y")
+
+
+def test_c5_long_context_reduced(F):
+    d = synth.workload(5, M=2048)
+    say(f"c5 M=2048 zero_rows={list(d['zero_rows'])} planted={d['planted']}")
+    x = O.bf16_to_f64(d["x"])
+    assert np.abs(x).max() > 448                       # saturation region present
+    cols = sample_idx(d["N"], 256, 55)
+    _linear_case(F, d["x"], d["w"], cols, what="c5")
+
+
+# ----------------------------------------------------------------------------
+# Full-size runs in the launch configuration the benchmark times
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("j", [0, 1, 2, 3])
+def test_c2_full_size_sampled(F, j):
+    d = synth.workload(2, j)
+    M, N = d["M"], d["N"]
+    say(f"c2 full {d['name']} {M}x{d['K']}->{N}")
+    rows = sample_idx(M, 48, 70 + j)
+    cols = sample_idx(N, 96, 80 + j)
+    x_d = dev_bf16(d["x"])
+    w_d = dev_bf16(d["w"])
+    qw_d, sw_d = F.fp8_quant_act(w_d)
+    y_d, qx_d, sx_d = F.fp8_linear(x_d, qw_d, sw_d)
+    torch.cuda.synchronize()
+    qw_o, sw_o = O.quant_per_row(d["w"][cols])
+    qx_o, sx_o = O.quant_per_row(d["x"][rows])
+    assert_codes_equal(qw_d.cpu().numpy()[cols], qw_o, "weight codes")
+    assert_scales_equal(sw_d.cpu().numpy()[cols], sw_o, "weight scales")
+    assert_codes_equal(qx_d.cpu().numpy()[rows], qx_o, "act codes")
+    assert_scales_equal(sx_d.cpu().numpy()[rows], sx_o, "act scales")
+    ysub = y_d[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()]
+    assert_y_close(host_bf16_f64(ysub), O.linear_per_channel(qx_o, sx_o, qw_o, sw_o), "y")
+
+
+def test_c5_full_size_sampled(F):
+    d = synth.workload(5)
+    M, N = d["M"], d["N"]
+    say(f"c5 full {M}x{d['K']}->{N} zero_rows={len(d['zero_rows'])}")
+    planted_rows = [p[0] for p in d["planted"]]
+    rows = np.unique(np.concatenate([sample_idx(M, 32, 90), d["zero_rows"][:4],
+                                     planted_rows]))
+    cols = sample_idx(N, 96, 91)
+    x_d = dev_bf16(d["x"])
+    w_d = dev_bf16(d["w"])
+    qw_d, sw_d = F.fp8_quant_act(w_d)
+    del w_d
+    y_d, qx_d, sx_d = F.fp8_linear(x_d, qw_d, sw_d)
+    torch.cuda.synchronize()
+    qx_o, sx_o = O.quant_per_row(d["x"][rows])
+    qw_o, sw_o = O.quant_per_row(d["w"][cols])
+    assert_codes_equal(qx_d.cpu().numpy()[rows], qx_o, "act codes")
+    assert_scales_equal(sx_d.cpu().numpy()[rows], sx_o, "act scales")
+    assert_codes_equal(qw_d.cpu().numpy()[cols], qw_o, "weight codes")
+    ysub = y_d[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()]
+    assert_y_close(host_bf16_f64(ysub), O.linear_per_channel(qx_o, sx_o, qw_o, sw_o), "y")
+    # properties over every row: zero rows -> s = 0 and an all-zero y row
+    sx_all = sx_d.cpu().numpy()
+    zr = torch.from_numpy(d["zero_rows"]).cuda()
+    assert np.all(sx_all[d["zero_rows"]] == 0)
+    assert int((y_d[zr] != 0).sum()) == 0
+    assert np.all(sx_all[np.setdiff1d(np.arange(M), d["zero_rows"])] > 0)
+
+
+# ----------------------------------------------------------------------------
+# Determinism and guard bands
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,K,flags", [(4096, 4096, 4096, 0), (16, 1024, 4096, 0),
+                                         (64, 8192, 8192, 0), (300, 1030, 1024, 2)])
+def test_deterministic(F, M, N, K, flags):
+    say(f"determinism {M}x{N}x{K} flags={flags}")
+    xb = synth.activations(M, K, 1, 2)
+    wb = synth.weights(N, K, 3)
+    qw, sw = F.fp8_quant_act(dev_bf16(wb))
+    x_d = dev_bf16(xb)
+    y1, q1, s1 = F.fp8_linear(x_d, qw, sw, flags=flags)
+    y2, q2, s2 = F.fp8_linear(x_d, qw, sw, flags=flags)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(q1, q2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+
+
+def test_guard_bands_untouched(F):
+    """Outputs written through views of larger buffers: bytes around them keep
+    their 0xA5 canary after quantization, GEMM (both paths) and linear."""
+    M, N, K = 70, 1030, 384
+    pad = 4096
+    xb = synth.activations(M, K, 7, 8)
+    wb = synth.weights(N, K, 9)
+    x_d = dev_bf16(xb)
+    qw, sw = F.fp8_quant_act(dev_bf16(wb))
+
+    def canvas(nbytes):
+        c = torch.full((nbytes + 2 * pad,), 0xA5, dtype=torch.uint8, device="cuda")
+        return c
+
+    for flags in (1, 2):
+        cy = canvas(M * N * 2)
+        cq = canvas(M * K)
+        cs = canvas(M * 4)
+        y = cy[pad:pad + M * N * 2].view(torch.bfloat16).view(M, N)
+        q = cq[pad:pad + M * K].view(M, K)
+        s = cs[pad:pad + M * 4].view(torch.float32)
+        F.fp8_linear(x_d, qw, sw, y=y, qx_out=q, sx_out=s, flags=flags)
+        torch.cuda.synchronize()
+        for c, n in ((cy, M * N * 2), (cq, M * K), (cs, M * 4)):
+            h = c.cpu().numpy()
+            assert np.all(h[:pad] == 0xA5) and np.all(h[pad + n:] == 0xA5), flags
+
+
+def test_empty_inputs(F):
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    q, s = F.fp8_quant_act(x)
+    assert q.shape == (0, 256) and s.shape == (0,)
+    qw = torch.zeros((128, 256), dtype=torch.uint8, device="cuda")
+    sw = torch.ones(128, dtype=torch.float32, device="cuda")
+    y, qx, sx = F.fp8_linear(x, qw, sw)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 128)
