@@ -15,9 +15,10 @@
 //  * the MFMA "A" operand is the weight tile and "B" the activation tile, so
 //    each lane's four results are four consecutive n of one row m and the
 //    epilogue stores 8 contiguous bytes per lane;
-//  * A/B tiles are staged global -> registers -> LDS, double buffered: the
-//    next K step's global loads are in flight while the current step's MFMAs
-//    run, one barrier per K step;
+//  * A/B tiles go straight from global memory to LDS (global_load_lds, 16 B
+//    per lane, no staging registers), double buffered: the next K step's
+//    loads are in flight while the current step's MFMAs run; each wave waits
+//    for its own loads (vmcnt) and one barrier per K step publishes them;
 //  * LDS rows are 128 bytes; 16-byte chunks are XOR-swizzled by the row so
 //    that the fragment reads (16 rows x one chunk per 16 lanes) hit distinct
 //    banks;
@@ -34,6 +35,11 @@ namespace {
 
 constexpr int BK = 128;
 constexpr int GM = 8;  // tile rows per L2 group
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt == 0 only.
+constexpr int kVmcnt0 = 0x0F70;
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(1))) void* gbl_ptr;
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
@@ -58,9 +64,9 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
     uint16_t* __restrict__ y, int M, int N, int K, int tiles_m, int tiles_n) {
   constexpr int TM = BM / 2, TN = BN / 2;
   constexpr int MJ = TM / 16, NI = TN / 16;
-  constexpr int XL = BM / 32, WL = BN / 32;  // 16-byte loads per thread
+  constexpr int XQ = BM / 32, WQ = BN / 32;  // 8-row groups per wave per stage
   constexpr int STAGE = (BM + BN) * BK;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   // ---- tile selection: XCD-aware remap, then grouped row-major order ----
   const int nblk = gridDim.x;
@@ -75,43 +81,39 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lr = lane & 15, kg = lane >> 4;
   const int wm = wave & 1, wn = wave >> 1;
 
-  // ---- global load addressing: thread -> (row, chunk) of each tile ----
-  const uint8_t* gx[XL];
-  const uint8_t* gw[WL];
-  int lx[XL], lw[WL];
+  // ---- direct global->LDS loads: a wave writes 1 KB = 8 tile rows per
+  // instruction, lane l to byte 16*l; lane l therefore fetches row l/8 of
+  // its group and the logical chunk whose swizzled slot is l % 8 ----
+  uint32_t xoff[XQ], woff[WQ];
 #pragma unroll
-  for (int i = 0; i < XL; ++i) {
-    const int id = tid + 256 * i, row = id >> 3, c = id & 7;
-    const int gr = min(m0 + row, M - 1);
-    gx[i] = qx + (int64_t)gr * K + c * 16;
-    lx[i] = lds_off(row, c);
+  for (int q = 0; q < XQ; ++q) {
+    const int g = q * 4 + wave, row = 8 * g + (lane >> 3);
+    const int c = (lane & 7) ^ swz(row);
+    xoff[q] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)K + (uint32_t)(c * 16);
   }
 #pragma unroll
-  for (int i = 0; i < WL; ++i) {
-    const int id = tid + 256 * i, row = id >> 3, c = id & 7;
-    const int gr = min(n0 + row, N - 1);
-    gw[i] = qw + (int64_t)gr * K + c * 16;
-    lw[i] = BM * BK + lds_off(row, c);
+  for (int q = 0; q < WQ; ++q) {
+    const int g = q * 4 + wave, row = 8 * g + (lane >> 3);
+    const int c = (lane & 7) ^ swz(row);
+    woff[q] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)K + (uint32_t)(c * 16);
   }
-
-  uint4 rx[XL], rw[WL];
-  auto gload = [&](int kt) {
-    const int64_t k0 = (int64_t)kt * BK;
+  auto issue = [&](int kt, int stage) {
+    const uint8_t* xk = qx + (size_t)kt * BK;
+    const uint8_t* wk = qw + (size_t)kt * BK;
+    uint8_t* sb = smem + stage * STAGE;
 #pragma unroll
-    for (int i = 0; i < XL; ++i) rx[i] = *reinterpret_cast<const uint4*>(gx[i] + k0);
+    for (int q = 0; q < XQ; ++q)
+      __builtin_amdgcn_global_load_lds((gbl_ptr)(xk + xoff[q]),
+                                       (lds_ptr)(sb + (q * 4 + wave) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < WL; ++i) rw[i] = *reinterpret_cast<const uint4*>(gw[i] + k0);
-  };
-  auto lstore = [&](int stage) {
-    uint8_t* base = smem + stage * STAGE;
-#pragma unroll
-    for (int i = 0; i < XL; ++i) *reinterpret_cast<uint4*>(base + lx[i]) = rx[i];
-#pragma unroll
-    for (int i = 0; i < WL; ++i) *reinterpret_cast<uint4*>(base + lw[i]) = rw[i];
+    for (int q = 0; q < WQ; ++q)
+      __builtin_amdgcn_global_load_lds((gbl_ptr)(wk + woff[q]),
+                                       (lds_ptr)(sb + BM * BK + (q * 4 + wave) * 1024), 16, 0, 0);
   };
 
   v4f acc[NI][MJ];
@@ -120,50 +122,71 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
 #pragma unroll
     for (int j = 0; j < MJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // block-variant scale addressing
+  // block-variant scales: row pointers of sx, weight-block row of this wave
   const int G = K / BK;
-  int mrow[MJ];
+  const float* sxr[MJ];
 #pragma unroll
-  for (int j = 0; j < MJ; ++j) mrow[j] = min(m0 + wm * TM + 16 * j + lr, M - 1);
-  const int wblk = (n0 + wn * TN) / 128;  // weight block row of this wave
+  for (int j = 0; j < MJ; ++j)
+    sxr[j] = sx + (size_t)min(m0 + wm * TM + 16 * j + lr, M - 1) * (BLOCK ? G : 1);
+  const float* swr = sw + (size_t)((n0 + wn * TN) / 128) * (BLOCK ? G : 1);
+  float sxc[MJ], sxn[MJ];
+  float swc = 0.f, swn = 0.f;
 
   const int KT = K / BK;
-  gload(0);
-  lstore(0);
+  if (BLOCK) {
+#pragma unroll
+    for (int j = 0; j < MJ; ++j) sxc[j] = sxr[j][0];
+    swc = swr[0];
+  }
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
 
   for (int kt = 0; kt < KT; ++kt) {
-    float sxg[MJ];
-    float swg = 0.f;
-    if (BLOCK) {
+    if (kt + 1 < KT) {
+      if (BLOCK) {  // next step's scales, issued before the tile loads
 #pragma unroll
-      for (int j = 0; j < MJ; ++j) sxg[j] = sx[(int64_t)mrow[j] * G + kt];
-      swg = sw[(int64_t)wblk * G + kt];
+        for (int j = 0; j < MJ; ++j) sxn[j] = sxr[j][kt + 1];
+        swn = swr[kt + 1];
+      }
+      issue(kt + 1, (kt + 1) & 1);
     }
-    if (kt + 1 < KT) gload(kt + 1);
 
     const uint8_t* sX = smem + (kt & 1) * STAGE;
     const uint8_t* sW = sX + BM * BK;
+    // Fragment schedule (pinned with scheduling barriers): A(0), then all B,
+    // then for each A block i: read A(i+1), run the MFMAs of A(i). Each
+    // MFMA group waits only for its own operands, and the next A fragment's
+    // LDS latency hides under the current group's MFMAs.
+    v8i a[2];
+    a[0] = lds_frag(sW, wn * TN + lr, kg);
     v8i b[MJ];
 #pragma unroll
     for (int j = 0; j < MJ; ++j) b[j] = lds_frag(sX, wm * TM + 16 * j + lr, kg);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const v8i a = lds_frag(sW, wn * TN + 16 * i + lr, kg);
+      if (i + 1 < NI) a[(i + 1) & 1] = lds_frag(sW, wn * TN + 16 * (i + 1) + lr, kg);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < MJ; ++j) {
         if (BLOCK) {
-          const v4f t = mfma_e4m3_16x16x128(a, b[j], v4f{0.f, 0.f, 0.f, 0.f});
-          const float sc = sxg[j] * swg;
+          const v4f t = mfma_e4m3_16x16x128(a[i & 1], b[j], v4f{0.f, 0.f, 0.f, 0.f});
+          const float sc = sxc[j] * swc;
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(t[r], sc, acc[i][j][r]);
         } else {
-          acc[i][j] = mfma_e4m3_16x16x128(a, b[j], acc[i][j]);
+          acc[i][j] = mfma_e4m3_16x16x128(a[i & 1], b[j], acc[i][j]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < KT) lstore((kt + 1) & 1);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);  // this wave's loads of step kt+1 landed
+    __syncthreads();                      // everyone's landed; step kt fully read
+    if (BLOCK) {
+#pragma unroll
+      for (int j = 0; j < MJ; ++j) sxc[j] = sxn[j];
+      swc = swn;
+    }
   }
 
   // ---- epilogue: scale, round to bf16, store 4 consecutive n per lane ----
@@ -232,9 +255,15 @@ void launch_gemm_prefill(const uint8_t* qx, const float* sx, const uint8_t* qw,
                          const float* sw, void* y, int64_t M, int64_t N,
                          int64_t K, bool block, hipStream_t st) {
   // 256 x 256 tiles halve the L2->CU traffic per flop against 256 x 128; use
-  // them when they still give at least two full waves of tiles on 256 CUs.
+  // them when they still fill the 256 CUs at least once.
   const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-  const bool use_big = big >= 512;
+#if defined(FP8DQ_TILE_OVERRIDE) && FP8DQ_TILE_OVERRIDE == 1
+  const bool use_big = true;
+#elif defined(FP8DQ_TILE_OVERRIDE) && FP8DQ_TILE_OVERRIDE == 2
+  const bool use_big = false;
+#else
+  const bool use_big = big >= 256;
+#endif
   if (block) {
     if (use_big) launch_cfg<256, 256, true>(qx, sx, qw, sw, y, M, N, K, st);
     else launch_cfg<256, 128, true>(qx, sx, qw, sw, y, M, N, K, st);
