@@ -37,6 +37,19 @@ __device__ __forceinline__ v4f mfma_e4m3_16x16x128(const v8i& a, const v8i& b,
                                                           0, 0);
 }
 
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// 32x32 output tile, K = 64 E4M3 x E4M3 products per MFMA, fp32 accumulate.
+// Operands: lane l holds row (l % 32) and 32 consecutive K-bytes, the two
+// lane halves l / 32 holding the two 32-byte K slices (same mapping for A
+// and B). Output: lane l holds C[8*(v/4) + 4*(l/32) + (v%4)][l % 32] in
+// element v = 0..15 (first index: A's rows, second: B's rows).
+__device__ __forceinline__ v16f mfma_e4m3_32x32x64(const v8i& a, const v8i& b,
+                                                   const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0,
+                                                          0, 0);
+}
+
 // fp32 -> bf16 bits, round to nearest even (inputs finite).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

@@ -29,14 +29,17 @@
 #include "kernels.hpp"
 
 #include <mutex>
+#include <type_traits>
 
 namespace fp8dq {
 namespace {
 
 constexpr int BK = 128;
 constexpr int GM = 8;  // tile rows per L2 group
-// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt == 0 only.
-constexpr int kVmcnt0 = 0x0F70;
+// s_waitcnt immediate (gfx9 encoding): wait until at most n vector-memory
+// operations of this wave are outstanding (expcnt / lgkmcnt not waited on).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+constexpr int kVmcnt0 = vmcnt_imm(0);
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(1))) void* gbl_ptr;
@@ -230,6 +233,225 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Deep-pipelined per-channel kernel: 256 x 256 tile, 64-byte K stages held in
+// an S-slot LDS ring (S * 32 KB), v_mfma_f32_32x32x64_f8f6f4.
+//  * loads for K step s are issued S-1 steps ahead with global_load_lds; a
+//    wave waits only for the oldest step it needs (partial vmcnt), so S-2
+//    steps of L2/MALL latency are covered;
+//  * the fragments of step kt+1 are read from LDS while step kt's 16 MFMAs
+//    run (two register sets); one barrier per step publishes step kt+1 and
+//    frees the slot that step kt+S-1 is loaded into;
+//  * the LDS loads are issued by a small asm helper (see dma16): the
+//    compiler then does not add its own all-loads wait before every LDS read
+//    (it cannot tell the ring slots apart), and the explicit vmcnt + barrier
+//    are the synchronization.
+// ---------------------------------------------------------------------------
+constexpr int DBK = 64;           // K bytes per stage
+constexpr int DROW = 64;          // LDS bytes per tile row
+constexpr int DTM = 128, DTN = 128;  // wave tile (m, n)
+constexpr int DMJ = DTM / 32, DNI = DTN / 32;
+constexpr int DXQ = 4, DWQ = 4;   // 16-row load groups per wave per stage
+constexpr int DLPS = DXQ + DWQ;   // loads per wave per stage
+
+__device__ __forceinline__ int dswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int dlds_off(int row, int c) {
+  return row * DROW + ((c ^ dswz(row)) << 4);
+}
+
+// One global_load_lds_dwordx4: 16 bytes from base + off (off per lane, base
+// wave-uniform) to LDS byte address lds + 16 * lane (lds wave-uniform). It
+// has no result registers; completion is observed with vmcnt. M0 carries the
+// LDS base and needs one wait state before the load reads it.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory", "m0");
+}
+
+template <int S>
+__global__ __launch_bounds__(256, 1) void gemm_prefill_deep_kernel(
+    const uint8_t* __restrict__ qx, const float* __restrict__ sx,
+    const uint8_t* __restrict__ qw, const float* __restrict__ sw,
+    uint16_t* __restrict__ y, int M, int N, int K, int tiles_m, int tiles_n) {
+  constexpr int BM = 256, BN = 256;
+  constexpr int STAGE = (BM + BN) * DBK;
+  constexpr int XB = BM * DBK;  // W tile offset inside a stage
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  const int nblk = gridDim.x;
+  int bid = blockIdx.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int group = GM * tiles_n;
+  const int first_m = (bid / group) * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int in_g = bid % group;
+  const int m0 = (first_m + in_g % gm) * BM;
+  const int n0 = (in_g / gm) * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int lr = lane & 31, kh = lane >> 5;
+
+  // lane l of a load writes LDS byte 16*l of a 1 KB group = row l/4, slot l%4
+  uint32_t xoff[DXQ], woff[DWQ];
+#pragma unroll
+  for (int q = 0; q < DXQ; ++q) {
+    const int row = 16 * (q * 4 + wave) + (lane >> 2);
+    const int c = (lane & 3) ^ dswz(row);
+    xoff[q] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)K + (uint32_t)(c * 16);
+  }
+#pragma unroll
+  for (int q = 0; q < DWQ; ++q) {
+    const int row = 16 * (q * 4 + wave) + (lane >> 2);
+    const int c = (lane & 3) ^ dswz(row);
+    woff[q] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)K + (uint32_t)(c * 16);
+  }
+  const int KT = K / DBK;  // even: K is a multiple of 128
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)smem;
+  // Load K step min(kt, KT-1) into ring slot kt % S. Past the end the last
+  // step is loaded again into a slot that is never read, which keeps the
+  // number of loads in flight (and so every wait count) constant.
+  auto issue = [&](int kt) {
+    const uint32_t sb = lds0 + (uint32_t)((kt % S) * STAGE) + wave * 1024;
+    const size_t k0 = (size_t)min(kt, KT - 1) * DBK;
+    const uint8_t* xb = qx + k0;
+    const uint8_t* wb = qw + k0;
+#pragma unroll
+    for (int q = 0; q < DXQ; ++q) dma16(xb, xoff[q], sb + q * 4096);
+#pragma unroll
+    for (int q = 0; q < DWQ; ++q) dma16(wb, woff[q], sb + XB + q * 4096);
+  };
+  const int arow0 = wn * DTN + lr, brow0 = wm * DTM + lr;
+  auto rd = [&](const uint8_t* base, int row) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(base + dlds_off(row, 2 * kh));
+    const uint4 hi = *reinterpret_cast<const uint4*>(base + dlds_off(row, 2 * kh + 1));
+    v8i r;
+    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+    return r;
+  };
+
+  v16f acc[DNI][DMJ];
+#pragma unroll
+  for (int i = 0; i < DNI; ++i)
+#pragma unroll
+    for (int j = 0; j < DMJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // prologue: steps 0 .. S-2 in flight; step 0 published and read
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(s);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * DLPS));
+  __syncthreads();
+  v8i A[2][DNI], B[2][DMJ];
+#pragma unroll
+  for (int i = 0; i < DNI; ++i) A[0][i] = rd(smem + XB, arow0 + 32 * i);
+#pragma unroll
+  for (int j = 0; j < DMJ; ++j) B[0][j] = rd(smem, brow0 + 32 * j);
+
+  // Step kt: wait until step kt+1 has landed (S-3 newer steps may still be
+  // in flight), publish it with the barrier (which also frees the slot step
+  // kt-1 used), refill that slot with step kt+S-1, then run step kt's 16
+  // MFMAs while reading step kt+1's fragments. MORE is false for the last.
+  auto step = [&](int kt, auto cur_c, auto more_c) {
+    constexpr int cur = decltype(cur_c)::value;
+    constexpr bool more = decltype(more_c)::value;
+    if (more) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 3) * DLPS));
+      __syncthreads();
+      issue(kt + S - 1);
+    }
+    const uint8_t* nX = smem + ((kt + 1) % S) * STAGE;
+    const uint8_t* nW = nX + XB;
+#pragma unroll
+    for (int i = 0; i < DNI; ++i) {
+#pragma unroll
+      for (int j = 0; j < DMJ; ++j) {
+        if (more) {
+          if (j == 0) A[cur ^ 1][i] = rd(nW, arow0 + 32 * i);
+          if (i == 0) B[cur ^ 1][j] = rd(nX, brow0 + 32 * j);
+        }
+        acc[i][j] = mfma_e4m3_32x32x64(A[cur][i], B[cur][j], acc[i][j]);
+      }
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  for (int kt = 0; kt < KT - 2; kt += 2) {
+    step(kt, I0(), std::true_type());
+    step(kt + 1, I1(), std::true_type());
+  }
+  step(KT - 2, I0(), std::true_type());
+  step(KT - 1, I1(), std::false_type());
+  // no load may still be writing this workgroup's LDS when it retires
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+  // ---- epilogue: lane holds row m, n = 8q + 4*(l/32) + r in each 32-block ----
+  const bool vec_ok = (N & 3) == 0;
+#pragma unroll
+  for (int j = 0; j < DMJ; ++j) {
+    const int m = m0 + wm * DTM + 32 * j + lr;
+    if (m >= M) continue;
+    const float sm = sx[m];
+#pragma unroll
+    for (int i = 0; i < DNI; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * DTN + 32 * i + 8 * q + 4 * kh;
+        float s4[4];
+        if (vec_ok && n + 3 < N) {
+          const float4 t = *reinterpret_cast<const float4*>(sw + n);
+          s4[0] = t.x; s4[1] = t.y; s4[2] = t.z; s4[3] = t.w;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s4[r] = (n + r < N) ? sw[n + r] : 0.f;
+        }
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r] * sm * s4[r];
+        uint16_t* out = y + (int64_t)m * N + n;
+        if (vec_ok && n + 3 < N) {
+          uint2 pk;
+          pk.x = pack_bf16x2(v[0], v[1]);
+          pk.y = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(out) = pk;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) out[r] = (uint16_t)f32_to_bf16_rne(v[r]);
+        }
+      }
+    }
+  }
+}
+
+template <int S>
+void launch_deep(const uint8_t* qx, const float* sx, const uint8_t* qw,
+                 const float* sw, void* y, int64_t M, int64_t N, int64_t K,
+                 hipStream_t st) {
+  constexpr int smem = S * (256 + 256) * DBK;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    (void)hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_prefill_deep_kernel<S>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  });
+  const int tiles_m = (int)((M + 255) / 256);
+  const int tiles_n = (int)((N + 255) / 256);
+  hipLaunchKernelGGL((gemm_prefill_deep_kernel<S>), dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(256), smem, st, qx, sx, qw, sw, (uint16_t*)y, (int)M,
+                     (int)N, (int)K, tiles_m, tiles_n);
+}
+
 template <int BM, int BN, bool BLOCK>
 void launch_cfg(const uint8_t* qx, const float* sx, const uint8_t* qw,
                 const float* sw, void* y, int64_t M, int64_t N, int64_t K,
@@ -268,8 +490,14 @@ void launch_gemm_prefill(const uint8_t* qx, const float* sx, const uint8_t* qw,
     if (use_big) launch_cfg<256, 256, true>(qx, sx, qw, sw, y, M, N, K, st);
     else launch_cfg<256, 128, true>(qx, sx, qw, sw, y, M, N, K, st);
   } else {
-    if (use_big) launch_cfg<256, 256, false>(qx, sx, qw, sw, y, M, N, K, st);
+#if defined(FP8DQ_TILE_OVERRIDE) && FP8DQ_TILE_OVERRIDE == 3
+    launch_cfg<256, 256, false>(qx, sx, qw, sw, y, M, N, K, st);
+#elif defined(FP8DQ_TILE_OVERRIDE) && FP8DQ_TILE_OVERRIDE == 4
+    launch_deep<4>(qx, sx, qw, sw, y, M, N, K, st);
+#else
+    if (use_big) launch_deep<5>(qx, sx, qw, sw, y, M, N, K, st);
     else launch_cfg<256, 128, false>(qx, sx, qw, sw, y, M, N, K, st);
+#endif
   }
 }
 
