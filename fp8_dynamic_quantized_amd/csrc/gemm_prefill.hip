@@ -249,15 +249,28 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
 //    are the synchronization.
 // ---------------------------------------------------------------------------
 constexpr int DBK = 64;           // K bytes per stage
-constexpr int DROW = 64;          // LDS bytes per tile row
-constexpr int DTM = 128, DTN = 128;  // wave tile (m, n)
-constexpr int DMJ = DTM / 32, DNI = DTN / 32;
-constexpr int DXQ = 4, DWQ = 4;   // 16-row load groups per wave per stage
-constexpr int DLPS = DXQ + DWQ;   // loads per wave per stage
 
-__device__ __forceinline__ int dswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// LDS layout of a stage tile (rows x four 16-byte K chunks), in 1 KB groups
+// of 16 rows. Inside a group, row r takes the 64-byte quad dq(r) (a fixed
+// permutation of the 16 rows) and chunk c the slot c ^ dh(r) of that quad.
+// Two properties follow:
+//  * a global_load_lds lane quad (4 consecutive lanes, 64 LDS bytes) holds
+//    the 4 chunks of one row: each quad fetches 64 contiguous global bytes;
+//  * the 16 pieces of every 16-lane phase of a 32x32x64 fragment read land
+//    on 16 different 16-byte bank slots (for each lane-phase grouping that
+//    the bank-conflict counter is consistent with), so reads are
+//    conflict-free.
+__device__ __forceinline__ int dq(int r) {   // row -> quad (local bits)
+  return (r & 1) | (((r >> 3) & 1) << 1) | (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 3);
+}
+__device__ __forceinline__ int dq_inv(int q) {  // quad -> local row
+  return (q & 1) | (((q >> 2) & 1) << 1) | (((q >> 3) & 1) << 2) | (((q >> 1) & 1) << 3);
+}
+__device__ __forceinline__ int dh(int r) {   // chunk permutation of row r
+  return (((r >> 1) ^ (r >> 4)) & 1) | (((r >> 2) & 1) << 1);
+}
 __device__ __forceinline__ int dlds_off(int row, int c) {
-  return row * DROW + ((c ^ dswz(row)) << 4);
+  return (row >> 4) * 1024 + ((dq(row & 15) << 2) + (c ^ dh(row))) * 16;
 }
 
 // One global_load_lds_dwordx4: 16 bytes from base + off (off per lane, base
@@ -274,12 +287,19 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
       : "memory", "m0");
 }
 
-template <int S>
-__global__ __launch_bounds__(256, 1) void gemm_prefill_deep_kernel(
+// BN: tile width (256 or 128); S: ring slots; WPC: workgroups per CU the
+// register / LDS budget is sized for (two let one workgroup's MFMAs cover the
+// other's barrier and memory waits).
+template <int BN, int S, int WPC>
+__global__ __launch_bounds__(256, WPC) void gemm_prefill_deep_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint8_t* __restrict__ qw, const float* __restrict__ sw,
     uint16_t* __restrict__ y, int M, int N, int K, int tiles_m, int tiles_n) {
-  constexpr int BM = 256, BN = 256;
+  constexpr int BM = 256;
+  constexpr int DTM = 128, DTN = BN / 2;          // wave tile (m, n)
+  constexpr int DMJ = DTM / 32, DNI = DTN / 32;   // 32x32 blocks per wave
+  constexpr int DXQ = BM / 64, DWQ = BN / 64;     // 16-row load groups / wave / stage
+  constexpr int DLPS = DXQ + DWQ;                 // loads per wave per stage
   constexpr int STAGE = (BM + BN) * DBK;
   constexpr int XB = BM * DBK;  // W tile offset inside a stage
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -300,43 +320,36 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_deep_kernel(
   const int wm = wave & 1, wn = wave >> 1;
   const int lr = lane & 31, kh = lane >> 5;
 
-  // lane l of a load writes LDS byte 16*l of a 1 KB group = row l/4, slot l%4
-  uint32_t xoff[DXQ], woff[DWQ];
+  // lane l of a load writes LDS byte 16*l of 1 KB group g (rows 16g..16g+15):
+  // quad l / 4 = row 16g + dq_inv(l / 4), slot l % 4 = chunk (l % 4) ^ dh(row)
+  uint32_t goff[DLPS];  // X groups first, then W groups
 #pragma unroll
-  for (int q = 0; q < DXQ; ++q) {
-    const int row = 16 * (q * 4 + wave) + (lane >> 2);
-    const int c = (lane & 3) ^ dswz(row);
-    xoff[q] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)K + (uint32_t)(c * 16);
-  }
-#pragma unroll
-  for (int q = 0; q < DWQ; ++q) {
-    const int row = 16 * (q * 4 + wave) + (lane >> 2);
-    const int c = (lane & 3) ^ dswz(row);
-    woff[q] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)K + (uint32_t)(c * 16);
+  for (int q = 0; q < DLPS; ++q) {
+    const bool isx = q < DXQ;
+    const int g = (isx ? q : q - DXQ) * 4 + wave;
+    const int row = 16 * g + dq_inv(lane >> 2);
+    const int c = (lane & 3) ^ dh(row);
+    const int grow = isx ? min(m0 + row, M - 1) : min(n0 + row, N - 1);
+    goff[q] = (uint32_t)grow * (uint32_t)K + (uint32_t)(c * 16);
   }
   const int KT = K / DBK;  // even: K is a multiple of 128
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)smem;
-  // Load K step min(kt, KT-1) into ring slot kt % S. Past the end the last
-  // step is loaded again into a slot that is never read, which keeps the
-  // number of loads in flight (and so every wait count) constant.
-  auto issue = [&](int kt) {
-    const uint32_t sb = lds0 + (uint32_t)((kt % S) * STAGE) + wave * 1024;
-    const size_t k0 = (size_t)min(kt, KT - 1) * DBK;
-    const uint8_t* xb = qx + k0;
-    const uint8_t* wb = qw + k0;
-#pragma unroll
-    for (int q = 0; q < DXQ; ++q) dma16(xb, xoff[q], sb + q * 4096);
-#pragma unroll
-    for (int q = 0; q < DWQ; ++q) dma16(wb, woff[q], sb + XB + q * 4096);
+  // Load q (0 .. DLPS-1) of K step min(kt, KT-1) into ring slot kt % S. Past
+  // the end the last step is loaded again into a slot that is never read,
+  // which keeps the number of loads in flight (and so every wait count)
+  // constant.
+  auto issue_one = [&](int kt, int q) {
+    const bool isx = q < DXQ;
+    const uint32_t sb = lds0 + (uint32_t)((kt % S) * STAGE) + (isx ? 0 : XB) +
+                        ((isx ? q : q - DXQ) * 4 + wave) * 1024;
+    const uint8_t* base = (isx ? qx : qw) + (size_t)min(kt, KT - 1) * DBK;
+    dma16(base, goff[q], sb);
   };
   const int arow0 = wn * DTN + lr, brow0 = wm * DTM + lr;
-  auto rd = [&](const uint8_t* base, int row) {
-    const uint4 lo = *reinterpret_cast<const uint4*>(base + dlds_off(row, 2 * kh));
-    const uint4 hi = *reinterpret_cast<const uint4*>(base + dlds_off(row, 2 * kh + 1));
-    v8i r;
-    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
-    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
-    return r;
+  // one 16-byte half (h = 0: chunk 2*kh, 1: chunk 2*kh+1) of a fragment
+  auto rd_half = [&](v8i& f, const uint8_t* base, int row, int h) {
+    const uint4 v = *reinterpret_cast<const uint4*>(base + dlds_off(row, 2 * kh + h));
+    f[4 * h + 0] = v.x; f[4 * h + 1] = v.y; f[4 * h + 2] = v.z; f[4 * h + 3] = v.w;
   };
 
   v16f acc[DNI][DMJ];
@@ -349,39 +362,54 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_deep_kernel(
 
   // prologue: steps 0 .. S-2 in flight; step 0 published and read
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s) issue(s);
+  for (int s = 0; s < S - 1; ++s)
+#pragma unroll
+    for (int q = 0; q < DLPS; ++q) issue_one(s, q);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * DLPS));
   __syncthreads();
   v8i A[2][DNI], B[2][DMJ];
 #pragma unroll
-  for (int i = 0; i < DNI; ++i) A[0][i] = rd(smem + XB, arow0 + 32 * i);
+  for (int i = 0; i < DNI; ++i) {
+    rd_half(A[0][i], smem + XB, arow0 + 32 * i, 0);
+    rd_half(A[0][i], smem + XB, arow0 + 32 * i, 1);
+  }
 #pragma unroll
-  for (int j = 0; j < DMJ; ++j) B[0][j] = rd(smem, brow0 + 32 * j);
+  for (int j = 0; j < DMJ; ++j) {
+    rd_half(B[0][j], smem, brow0 + 32 * j, 0);
+    rd_half(B[0][j], smem, brow0 + 32 * j, 1);
+  }
 
   // Step kt: wait until step kt+1 has landed (S-3 newer steps may still be
   // in flight), publish it with the barrier (which also frees the slot step
-  // kt-1 used), refill that slot with step kt+S-1, then run step kt's 16
-  // MFMAs while reading step kt+1's fragments. MORE is false for the last.
+  // kt-1 used), then issue step kt's MFMAs in a fixed order, each paired
+  // with one 16-byte fragment read of step kt+1 and the first ones with one
+  // refill load of step kt+S-1. Scheduling barriers keep that interleave:
+  // the LDS latency of every read hides under the MFMAs of the current step.
+  constexpr int NM = DNI * DMJ;          // MFMAs per step
+  constexpr int NR = 2 * (DNI + DMJ);    // fragment halves per step
+  static_assert(NR <= NM && DLPS <= NM, "one read / load per MFMA at most");
   auto step = [&](int kt, auto cur_c, auto more_c) {
     constexpr int cur = decltype(cur_c)::value;
     constexpr bool more = decltype(more_c)::value;
     if (more) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 3) * DLPS));
       __syncthreads();
-      issue(kt + S - 1);
     }
     const uint8_t* nX = smem + ((kt + 1) % S) * STAGE;
     const uint8_t* nW = nX + XB;
 #pragma unroll
-    for (int i = 0; i < DNI; ++i) {
-#pragma unroll
-      for (int j = 0; j < DMJ; ++j) {
-        if (more) {
-          if (j == 0) A[cur ^ 1][i] = rd(nW, arow0 + 32 * i);
-          if (i == 0) B[cur ^ 1][j] = rd(nX, brow0 + 32 * j);
+    for (int t = 0; t < NM; ++t) {
+      if (more) {
+        if (t < NR) {
+          const int f = t >> 1, h = t & 1;
+          if (f < DNI) rd_half(A[cur ^ 1][f], nW, arow0 + 32 * f, h);
+          else rd_half(B[cur ^ 1][f - DNI], nX, brow0 + 32 * (f - DNI), h);
         }
-        acc[i][j] = mfma_e4m3_32x32x64(A[cur][i], B[cur][j], acc[i][j]);
+        if (t < DLPS) issue_one(kt + S - 1, t);
       }
+      const int i = t / DMJ, j = t % DMJ;
+      acc[i][j] = mfma_e4m3_32x32x64(A[cur][i], B[cur][j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   using I0 = std::integral_constant<int, 0>;
@@ -434,20 +462,21 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_deep_kernel(
   }
 }
 
-template <int S>
+template <int BN, int S, int WPC>
 void launch_deep(const uint8_t* qx, const float* sx, const uint8_t* qw,
                  const float* sw, void* y, int64_t M, int64_t N, int64_t K,
                  hipStream_t st) {
-  constexpr int smem = S * (256 + 256) * DBK;
+  constexpr int smem = S * (256 + BN) * DBK;
+  static_assert(smem * WPC <= 160 * 1024, "LDS budget");
   static std::once_flag once;
   std::call_once(once, [] {
     (void)hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_prefill_deep_kernel<S>),
+        reinterpret_cast<const void*>(&gemm_prefill_deep_kernel<BN, S, WPC>),
         hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   });
   const int tiles_m = (int)((M + 255) / 256);
-  const int tiles_n = (int)((N + 255) / 256);
-  hipLaunchKernelGGL((gemm_prefill_deep_kernel<S>), dim3((unsigned)(tiles_m * tiles_n)),
+  const int tiles_n = (int)((N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_prefill_deep_kernel<BN, S, WPC>), dim3((unsigned)(tiles_m * tiles_n)),
                      dim3(256), smem, st, qx, sx, qw, sw, (uint16_t*)y, (int)M,
                      (int)N, (int)K, tiles_m, tiles_n);
 }
@@ -491,11 +520,13 @@ void launch_gemm_prefill(const uint8_t* qx, const float* sx, const uint8_t* qw,
     else launch_cfg<256, 128, true>(qx, sx, qw, sw, y, M, N, K, st);
   } else {
 #if defined(FP8DQ_TILE_OVERRIDE) && FP8DQ_TILE_OVERRIDE == 3
-    launch_cfg<256, 256, false>(qx, sx, qw, sw, y, M, N, K, st);
+    launch_deep<128, 4, 1>(qx, sx, qw, sw, y, M, N, K, st);
 #elif defined(FP8DQ_TILE_OVERRIDE) && FP8DQ_TILE_OVERRIDE == 4
-    launch_deep<4>(qx, sx, qw, sw, y, M, N, K, st);
+    launch_deep<128, 6, 1>(qx, sx, qw, sw, y, M, N, K, st);
+#elif defined(FP8DQ_TILE_OVERRIDE) && FP8DQ_TILE_OVERRIDE == 5
+    launch_deep<256, 4, 1>(qx, sx, qw, sw, y, M, N, K, st);
 #else
-    if (use_big) launch_deep<5>(qx, sx, qw, sw, y, M, N, K, st);
+    if (use_big) launch_deep<256, 5, 1>(qx, sx, qw, sw, y, M, N, K, st);
     else launch_cfg<256, 128, false>(qx, sx, qw, sw, y, M, N, K, st);
 #endif
   }
