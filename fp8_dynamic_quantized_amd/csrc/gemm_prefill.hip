@@ -249,6 +249,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
 //    are the synchronization.
 // ---------------------------------------------------------------------------
 constexpr int DBK = 64;           // K bytes per stage
+constexpr int DEPI = 264;         // LDS row stride (bytes) of the epilogue staging
 
 // LDS layout of a stage tile (rows x four 16-byte K chunks), in 1 KB groups
 // of 16 rows. Inside a group, row r takes the 64-byte quad dq(r) (a fixed
@@ -423,40 +424,57 @@ __global__ __launch_bounds__(256, WPC) void gemm_prefill_deep_kernel(
   // no load may still be writing this workgroup's LDS when it retires
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  // ---- epilogue: lane holds row m, n = 8q + 4*(l/32) + r in each 32-block ----
-  const bool vec_ok = (N & 3) == 0;
+  // ---- epilogue: scale, round to bf16, stage through LDS, coalesced store --
+  // Each wave writes its DTM x DTN bf16 block to its own LDS area (row stride
+  // DEPI bytes: 8-byte writes from 32 consecutive rows fall on distinct
+  // banks), then stores it row-wise, 16 bytes per lane: every store
+  // instruction covers whole 256-byte row segments.
+  __syncthreads();  // every wave is done reading the ring
+  uint8_t* ep = smem + wave * (DTM * DEPI);
 #pragma unroll
   for (int j = 0; j < DMJ; ++j) {
-    const int m = m0 + wm * DTM + 32 * j + lr;
-    if (m >= M) continue;
-    const float sm = sx[m];
+    const int ml = 32 * j + lr;
+    const float sm = sx[min(m0 + wm * DTM + ml, M - 1)];
 #pragma unroll
     for (int i = 0; i < DNI; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * DTN + 32 * i + 8 * q + 4 * kh;
+        const int nl = 32 * i + 8 * q + 4 * kh;
+        const int n = n0 + wn * DTN + nl;
         float s4[4];
-        if (vec_ok && n + 3 < N) {
+        if (n + 3 < N) {
           const float4 t = *reinterpret_cast<const float4*>(sw + n);
           s4[0] = t.x; s4[1] = t.y; s4[2] = t.z; s4[3] = t.w;
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) s4[r] = (n + r < N) ? sw[n + r] : 0.f;
         }
-        float v[4];
+        uint2 pk;
+        pk.x = pack_bf16x2(acc[i][j][4 * q + 0] * sm * s4[0], acc[i][j][4 * q + 1] * sm * s4[1]);
+        pk.y = pack_bf16x2(acc[i][j][4 * q + 2] * sm * s4[2], acc[i][j][4 * q + 3] * sm * s4[3]);
+        *reinterpret_cast<uint2*>(ep + ml * DEPI + nl * 2) = pk;
+      }
+    }
+  }
+  const int rsub = lane >> 4, cseg = lane & 15;  // 4 rows x 16 segments of 16 B
+  const int nbase = n0 + wn * DTN + 8 * cseg;
+  const bool vec_ok = (N & 7) == 0 && nbase + 7 < N;
+#pragma unroll 4
+  for (int t = 0; t < DTM / 4; ++t) {
+    const int ml = 4 * t + rsub;
+    const int m = m0 + wm * DTM + ml;
+    const uint8_t* src = ep + ml * DEPI + cseg * 16;
+    const uint2 lo = *reinterpret_cast<const uint2*>(src);
+    const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
+    if (m < M) {
+      uint16_t* out = y + (int64_t)m * N + nbase;
+      if (vec_ok) {
+        *reinterpret_cast<uint4*>(out) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      } else {
+        const uint32_t w4[4] = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r] * sm * s4[r];
-        uint16_t* out = y + (int64_t)m * N + n;
-        if (vec_ok && n + 3 < N) {
-          uint2 pk;
-          pk.x = pack_bf16x2(v[0], v[1]);
-          pk.y = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<uint2*>(out) = pk;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < N) out[r] = (uint16_t)f32_to_bf16_rne(v[r]);
-        }
+        for (int e = 0; e < 8; ++e)
+          if (nbase + e < N) out[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
       }
     }
   }
@@ -466,7 +484,9 @@ template <int BN, int S, int WPC>
 void launch_deep(const uint8_t* qx, const float* sx, const uint8_t* qw,
                  const float* sw, void* y, int64_t M, int64_t N, int64_t K,
                  hipStream_t st) {
-  constexpr int smem = S * (256 + BN) * DBK;
+  constexpr int ring = S * (256 + BN) * DBK;
+  constexpr int stage_out = 4 * 128 * DEPI;  // epilogue staging, 4 waves
+  constexpr int smem = ring > stage_out ? ring : stage_out;
   static_assert(smem * WPC <= 160 * 1024, "LDS budget");
   static std::once_flag once;
   std::call_once(once, [] {
