@@ -21,7 +21,9 @@
 //    Such lanes -- and lanes in the E4M3 subnormal range, where the midpoint
 //    test below does not apply -- take an exact fix-up: the sign of
 //    (midpoint * s - |x|) from one fused multiply-add decides the side (and
-//    exactly zero means a tie, resolved to the even code).
+//    exactly zero means a tie, resolved to the even code). bf16 inputs make
+//    exact ties common (a row whose amax has a short mantissa puts many x / s
+//    exactly on midpoints), so the fix-up is inline and branch-free.
 //  * exact quotients never exceed 448.9 for bf16 inputs (the scale rounding
 //    moves them by at most a few parts per thousand, in the fp32-subnormal
 //    scale range), so y stays below 464, where the hardware conversion still
@@ -34,27 +36,33 @@
 namespace fp8dq {
 namespace {
 
-constexpr uint32_t kNearTol = 4;          // fp32 ulps of slack around a midpoint
+constexpr uint32_t kNearTol = 2;          // fp32 ulps of slack around a midpoint
 constexpr float kTinyScale = 0x1p-64f;    // scales below this are pre-scaled
 constexpr float kPreScale = 0x1p64f;
 
-// Exact E4M3 magnitude code of |x| / s given the fast candidate code.
-//   ax  : |x| (times the pre-scale p)    sp : s * p
-//   ay  : |y|, the fp32 estimate of |x| / s     c : candidate magnitude code
-__device__ __noinline__ uint32_t exact_code(float ax, float sp, float ay,
-                                            uint32_t c) {
-  float cv = __builtin_amdgcn_cvt_f32_fp8(c, 0);
-  if (ay == cv) return c;  // on a grid point: far from every midpoint
-  bool up = ay > cv;
-  if (up && c == 126u) return 126u;  // beyond 448: saturate
-  uint32_t c2 = up ? c + 1u : c - 1u;
-  float v2 = __builtin_amdgcn_cvt_f32_fp8(c2, 0);
-  float mid = 0.5f * (cv + v2);       // exact: at most five significant bits
-  float t = __builtin_fmaf(mid, sp, -ax);  // sign(mid*s - |x|), exact
-  uint32_t lo = up ? c : c2, hi = up ? c2 : c;
-  if (t > 0.0f) return lo;
-  if (t < 0.0f) return hi;
-  return (lo & 1u) ? hi : lo;  // exact tie: even code
+// Exact E4M3 magnitude code of |x| / s, given its fp32 estimate ay = |y|
+// (within 2 fp32 ulps). The exact quotient lies in the E4M3 interval that
+// truncation of ay selects, or just across its midpoint; one fused
+// multiply-add gives the exact sign of (midpoint * s - |x|): positive keeps
+// the lower code, negative takes the upper one, zero is a tie that goes to
+// the even code. Normal range: the interval comes from ay's bits; E4M3
+// subnormal range (ay < 2^-6): the spacing is 2^-9.
+//   ax = |x| (times the pre-scale p), sp = s * p.
+__device__ __forceinline__ uint32_t exact_mag(float ax, float sp, float ay) {
+  const uint32_t yb = __float_as_uint(ay);
+  uint32_t trunc;
+  float mid;
+  if (ay >= 0x1p-6f) {
+    trunc = (yb >> 20) - (120u << 3);  // exponent rebias 127 -> 7, 3 bits kept
+    mid = __uint_as_float((yb & 0xFFF00000u) | 0x80000u);
+  } else {
+    trunc = (uint32_t)(ay * 512.0f);   // floor: ay >= 0
+    mid = __builtin_fmaf((float)trunc, 0x1p-9f, 0x1p-10f);
+  }
+  const float t = __builtin_fmaf(mid, sp, -ax);
+  const uint32_t up = (t < 0.0f) | ((t == 0.0f) & (trunc & 1u));
+  const uint32_t code = trunc + up;
+  return code < 126u ? code : 126u;  // beyond 448: saturate
 }
 
 // True when y needs the exact fix-up: its low 20 mantissa bits are within
@@ -89,9 +97,8 @@ __device__ __forceinline__ uint2 quant8(uint4 raw, float s, float r, float p) {
     if (needs_fixup(y[i])) {
       uint32_t& word = (i < 4) ? lo : hi;
       const int sh = 8 * (i & 3);
-      uint32_t cand = (word >> sh) & 0x7Fu;
       float ax = __builtin_fabsf(PRE ? x[i] * p : x[i]);
-      uint32_t mag = exact_code(ax, sp, __builtin_fabsf(y[i]), cand);
+      uint32_t mag = exact_mag(ax, sp, __builtin_fabsf(y[i]));
       uint32_t code = mag | ((__float_as_uint(x[i]) >> 24) & 0x80u);
       word = (word & ~(0xFFu << sh)) | (code << sh);
     }
