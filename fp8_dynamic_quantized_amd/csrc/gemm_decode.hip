@@ -27,6 +27,14 @@ namespace {
 
 constexpr int BK = 128;
 
+// Compile-time tunables (defaults are the tuned values).
+#ifndef FP8DQ_DEC_D
+#define FP8DQ_DEC_D 4      // K steps of fragments in flight per wave
+#endif
+#ifndef FP8DQ_DEC_NT
+#define FP8DQ_DEC_NT 0     // non-temporal weight loads (measured slower)
+#endif
+
 __device__ __forceinline__ v8i gload_frag_nt(const uint8_t* p) {
   const uint4 lo = ld16_nt(p);
   const uint4 hi = ld16_nt(p + 16);
@@ -87,7 +95,8 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
   auto load = [&](int d, int t) {
     const int64_t k0 = (int64_t)(first + 4 * t) * BK;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) a[d][i] = gload_frag_nt(wp[i] + k0);
+    for (int i = 0; i < NB; ++i)
+      a[d][i] = FP8DQ_DEC_NT ? gload_frag_nt(wp[i] + k0) : gload_frag(wp[i] + k0);
 #pragma unroll
     for (int j = 0; j < MB; ++j) b[d][j] = gload_frag(xp[j] + k0);
   };
@@ -224,8 +233,9 @@ template <int MB, bool BLOCK>
 void launch_mb(const uint8_t* qx, const float* sx, const uint8_t* qw,
                const float* sw, void* y, float* ws, int64_t M, int64_t N,
                int64_t K, const DecodePlan& p, hipStream_t st) {
-  if (p.nb == 1) launch_cfg<MB, 1, 4, BLOCK>(qx, sx, qw, sw, y, ws, M, N, K, p, st);
-  else launch_cfg<MB, 2, 4, BLOCK>(qx, sx, qw, sw, y, ws, M, N, K, p, st);
+  if (p.nb == 1) launch_cfg<MB, 1, FP8DQ_DEC_D, BLOCK>(qx, sx, qw, sw, y, ws, M, N, K, p, st);
+  else if (p.nb == 2) launch_cfg<MB, 2, FP8DQ_DEC_D, BLOCK>(qx, sx, qw, sw, y, ws, M, N, K, p, st);
+  else launch_cfg<MB, 4, FP8DQ_DEC_D, BLOCK>(qx, sx, qw, sw, y, ws, M, N, K, p, st);
 }
 
 }  // namespace
@@ -235,10 +245,14 @@ DecodePlan plan_decode(int64_t M, int64_t N, int64_t K) {
   p.mb = (int)((M + 15) / 16);
   if (p.mb < 1) p.mb = 1;
   if (p.mb > 4) p.mb = 4;  // callers guarantee M <= 64 on this path
-  // Two weight row-blocks per workgroup when N alone yields plenty of
-  // workgroups (halves the activation re-reads per weight byte).
   const int64_t KT = K / BK;
-  p.nb = (N / 32 >= 1024) ? 2 : 1;
+#ifdef FP8DQ_DEC_NB
+  p.nb = FP8DQ_DEC_NB;
+#else
+  // Two weight row-blocks per workgroup halve the activation re-reads per
+  // weight byte (worth it from M > 16) and suit very wide layers.
+  p.nb = (M > 16 || N / 32 >= 1024) ? 2 : 1;
+#endif
   const int64_t wgs = (N + 16 * p.nb - 1) / (16 * p.nb);
   // Split K across the grid until there are >= 512 workgroups, keeping at
   // least 8 K steps (2 per wave) in each slice.

@@ -133,12 +133,12 @@ __device__ __forceinline__ void unit_scale(uint32_t amax_bits, float& s,
 // in registers. Block = 256 threads (4 / TEAM_WAVES rows per block).
 // ---------------------------------------------------------------------------
 template <int CH, int TEAM_WAVES>
-__global__ __launch_bounds__(256) void quant_rows_kernel(
+__global__ __launch_bounds__(TEAM_WAVES >= 4 ? 64 * TEAM_WAVES : 256) void quant_rows_kernel(
     const uint4* __restrict__ x, int64_t rows, int64_t K, uint2* __restrict__ q,
     float* __restrict__ scale) {
   constexpr int TEAM = 64 * TEAM_WAVES;
-  constexpr int ROWS_PER_BLOCK = 4 / TEAM_WAVES;
-  __shared__ uint32_t red[4];
+  constexpr int ROWS_PER_BLOCK = TEAM_WAVES >= 4 ? 1 : 4 / TEAM_WAVES;
+  __shared__ uint32_t red[TEAM_WAVES >= 4 ? TEAM_WAVES : 4];
   const int tid = threadIdx.x;
   const int team = tid / TEAM;
   const int tl = tid % TEAM;
@@ -294,10 +294,11 @@ __global__ __launch_bounds__(256) void quant_wblock_kernel(
 template <int CH, int TW>
 void launch_rows(const void* x, int64_t rows, int64_t K, uint8_t* q,
                  float* scale, hipStream_t st) {
-  constexpr int RPB = 4 / TW;
+  constexpr int RPB = TW >= 4 ? 1 : 4 / TW;
+  constexpr int THREADS = TW >= 4 ? 64 * TW : 256;
   const int64_t blocks = (rows + RPB - 1) / RPB;
   hipLaunchKernelGGL((quant_rows_kernel<CH, TW>), dim3((unsigned)blocks),
-                     dim3(256), 0, st, (const uint4*)x, rows, K, (uint2*)q,
+                     dim3(THREADS), 0, st, (const uint4*)x, rows, K, (uint2*)q,
                      scale);
 }
 
@@ -307,6 +308,14 @@ void launch_rows(const void* x, int64_t rows, int64_t K, uint8_t* q,
 void launch_quant_rows(const void* x, int64_t rows, int64_t K, uint8_t* q,
                        float* scale, hipStream_t st) {
   const int64_t nch = K / 8;
+  // Few rows (decode): a 1024-thread block per row, each thread 1-4 chunks,
+  // so the load -> amax -> quantize chain of one row is short.
+  if (rows <= 128 && nch > 64 && nch <= 1024 * 4) {
+    if (nch <= 1024) launch_rows<1, 16>(x, rows, K, q, scale, st);
+    else if (nch <= 2048) launch_rows<2, 16>(x, rows, K, q, scale, st);
+    else launch_rows<4, 16>(x, rows, K, q, scale, st);
+    return;
+  }
   // One wave per row while the row fits 16 chunks per lane, else 4 waves.
   if (nch <= 64 * 1) launch_rows<1, 1>(x, rows, K, q, scale, st);
   else if (nch <= 64 * 2) launch_rows<2, 1>(x, rows, K, q, scale, st);
