@@ -10,13 +10,29 @@ channel, before timing (static weights). Inputs are seeded synthetic data
 resident in HBM.
 
 Prints one JSON line (value = whole-step TFLOP/s, 2*M*N*K per linear).
-Also reported: the roofline of the dominant kernel (the gate_up GEMM,
-timed with HIP events on the stream it runs on), per-linear kernel times,
-and the CPU oracle timed on a bounded sample of the same workload.
+Also reported:
+  roofline      the dominant kernel (the gate_up GEMM), timed with HIP events
+                on the stream it runs on; HBM traffic from the committed
+                counter summary when it matches the current kernel source;
+  per_linear    per-linear quantizer and GEMM kernel times;
+  decode        the Llama-3.1-70B decode linears at M in {1, 8, 32, 64}:
+                end-to-end fp8_linear weight GB/s with cold weights
+                (rotated copies well beyond the 256 MB last-level cache);
+  cpu_baseline  the CPU oracle timed on a bounded sample of the workload.
+
+Other modes (profiling helpers, no JSON line):
+  --copy-calibration        a plain 1 GiB device copy, three times, for
+                            scaling the FETCH_SIZE / WRITE_SIZE counters;
+  --summarize-profile DIR   per-kernel, per-grid duration / counter summary
+                            of a rocprofv3 csv output directory.
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -28,6 +44,11 @@ sys.path.insert(0, ROOT)
 METRIC = "FP8-dynamic linear TFLOP/s (prefill) + weight GB/s (decode), % of roofline"
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+DOM_KERNEL = "gemm_prefill_deep_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_prefill_deep_gate_up_m4096_traffic.txt")
+KERNEL_SOURCES = ["fp8_dynamic_quantized_amd/csrc/gemm_prefill.hip",
+                  "fp8_dynamic_quantized_amd/csrc/device_common.hpp"]
+COPY_BYTES = 1 << 30
 
 
 def log(*a):
@@ -39,7 +60,32 @@ def to_dev(bits, torch):
         torch.bfloat16).cuda()
 
 
-def cpu_baseline(shapes, M, rows, col_frac):
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when it is absent or was taken on other kernel source."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(shapes, rows, col_frac):
     """The oracle (as it stands) on a bounded sample: `rows` tokens x
     N*col_frac output channels of each linear; weights quantized before
     timing, as on the GPU."""
@@ -73,38 +119,11 @@ def cpu_baseline(shapes, M, rows, col_frac):
                       f"quantization before timing; host cores {os.cpu_count()}"}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-rows", type=int, default=1024,
-                    help="token rows of the CPU-oracle sample")
-    ap.add_argument("--cpu-col-frac", type=float, default=0.25,
-                    help="fraction of output channels in the CPU-oracle sample")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args()
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py: this benchmark runs on one GPU only (got --gpus {args.gpus}, "
-              f"WORLD_SIZE {world}); multi-GPU scaling is not part of this build.",
-              file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-
-    import fp8_dynamic_quantized_amd as F
+def bench_prefill(F, torch, steps, warmup):
     import synth
-    from fp8_dynamic_quantized_amd import build as B
-    if not os.path.exists(B.LIB):
-        B.build()
-    F.lib()
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-
     shapes = synth.SHAPES["c2"]
     M = synth.M_OF["c2"][0]
-    log(f"setup: {len(shapes)} linears, M={M}")
+    log(f"prefill setup: {len(shapes)} linears, M={M}")
     layers = []
     for j, (name, K, N) in enumerate(shapes):
         d = synth.workload(2, j)
@@ -120,39 +139,40 @@ def main():
         })
     torch.cuda.synchronize()
     flops_step = sum(2 * M * L["N"] * L["K"] for L in layers)
+    stream = torch.cuda.current_stream()        # the stream every launch uses
 
     def step(ev=None):
         for i, L in enumerate(layers):
             if ev is not None:
-                ev[i][0].record()
+                ev[i][0].record(stream)
             F.fp8_quant_act(L["x"], q=L["qx"], scale=L["sx"])
             if ev is not None:
-                ev[i][1].record()
+                ev[i][1].record(stream)
             F.fp8_gemm(L["qx"], L["sx"], L["qw"], L["sw"], y=L["y"])
             if ev is not None:
-                ev[i][2].record()
+                ev[i][2].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            for _ in layers] for _ in range(args.steps)]
+            for _ in layers] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
+    for k in range(steps):
         step(evs[k])
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
 
     quant_ms = np.zeros(len(layers))
     gemm_ms = np.zeros(len(layers))
-    for k in range(args.steps):
+    for k in range(steps):
         for i in range(len(layers)):
             quant_ms[i] += evs[k][i][0].elapsed_time(evs[k][i][1])
             gemm_ms[i] += evs[k][i][1].elapsed_time(evs[k][i][2])
-    quant_ms /= args.steps
-    gemm_ms /= args.steps
+    quant_ms /= steps
+    gemm_ms /= steps
 
     per_layer = {}
     for i, L in enumerate(layers):
@@ -167,16 +187,165 @@ def main():
     dom = [i for i, L in enumerate(layers) if L["name"] == "gate_up"][0]
     Ld = layers[dom]
     achieved = 2 * M * Ld["N"] * Ld["K"] / (gemm_ms[dom] * 1e-3) / 1e12
-    value = flops_step * args.steps / dt / 1e12
+    res = {"M": M, "shapes": [[L["name"], L["K"], L["N"]] for L in layers],
+           "value": flops_step * steps / dt / 1e12, "ms_per_step": dt / steps * 1e3,
+           "achieved": achieved, "dom_us": gemm_ms[dom] * 1e3,
+           "dom_shape": (M, Ld["K"], Ld["N"]), "per_layer": per_layer}
+    del layers
+    torch.cuda.empty_cache()
+    return res
 
+
+def bench_decode(F, torch, batches=7, per_batch=20, warm=5):
+    """fp8_linear on the 70B decode shapes, cold weights: enough distinct
+    copies of the quantized weight rotate through to exceed 2 GB."""
+    import synth
+    stream = torch.cuda.current_stream()
+    out = {}
+    fracs = []
+    for j, (name, K, N) in enumerate(synth.SHAPES["c3"]):
+        log(f"decode setup: {name} {K}->{N}")
+        w = to_dev(synth.workload(3, j, x=False)["w"], torch)
+        qw, sw = F.fp8_quant_act(w)
+        del w
+        wbytes = N * K + 4 * N
+        copies = max(2, -(-(2 << 30) // wbytes) + 1)
+        qws = [qw] + [qw.clone() for _ in range(copies - 1)]
+        for i, M in enumerate(synth.M_OF["c3"]):
+            x = to_dev(synth.workload(3, j, i, w=False)["x"], torch)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            qx = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+            sx = torch.empty((M,), dtype=torch.float32, device="cuda")
+            need = F.fp8_workspace_bytes(M, N, K)
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+            c = [0]
+
+            def run():
+                F.fp8_linear(x, qws[c[0] % copies], sw, y=y, qx_out=qx, sx_out=sx, ws=ws)
+                c[0] += 1
+            for _ in range(warm):
+                run()
+            times = []
+            for _ in range(batches):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(per_batch):
+                    run()
+                e1.record(stream)
+                e1.synchronize()
+                times.append(e0.elapsed_time(e1) * 1e3 / per_batch)
+            times.sort()
+            us = statistics.median(times)
+            gbs = wbytes / (us * 1e-6) / 1e9
+            fracs.append(gbs / PEAK_HBM_GBS)
+            out[f"{name}_M{M}"] = {
+                "us": round(us, 2), "p10_us": round(times[0], 2),
+                "p90_us": round(times[-1], 2), "weight_gbs": round(gbs, 1),
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+            log(f"  M={M}: {us:.1f} us, weight {gbs:.0f} GB/s")
+            del x, y, qx, sx, ws
+        del qws, qw, sw
+        torch.cuda.empty_cache()
+    out["mean_frac"] = round(float(np.mean(fracs)), 4)
+    out["protocol"] = (f"fp8_linear end-to-end (quantize + GEMM [+ split-K reduce]); "
+                       f"median of {batches} batches of {per_batch} launches after "
+                       f"{warm} warm-ups; weight copies rotated, >2 GB per shape; "
+                       f"weight bytes = N*K + 4*N")
+    return out
+
+
+def copy_calibration(torch):
+    src = torch.randint(0, 255, (COPY_BYTES,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
+
+
+def summarize_profile(d):
+    """Print per-kernel, per-grid-size averages of a rocprofv3 csv directory
+    (kernel trace and/or counter collection)."""
+    rows = []
+    for p in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                rows.append((r["Kernel_Name"], int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"])
+                             * int(r["Grid_Size_Z"]),
+                             int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    if rows:
+        agg = {}
+        for name, grid, ns in rows:
+            agg.setdefault((name, grid), []).append(ns)
+        print(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'grid':>10}  kernel")
+        for (name, grid), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+            print(f"{len(v):6d} {np.mean(v) / 1e3:10.2f} {min(v) / 1e3:10.2f} "
+                  f"{max(v) / 1e3:10.2f} {grid:10d}  {name[:110]}")
+    for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        agg = {}
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                key = (r["Kernel_Name"], int(r["Grid_Size"]), r["Counter_Name"])
+                agg.setdefault(key, []).append(float(r["Counter_Value"]))
+        print(f"{'calls':>6} {'avg':>14} {'grid':>10} {'counter':>12}  kernel")
+        for (name, grid, cn), v in sorted(agg.items()):
+            print(f"{len(v):6d} {np.mean(v):14.2f} {grid:10d} {cn:>12}  {name[:110]}")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="token rows of the CPU-oracle sample")
+    ap.add_argument("--cpu-col-frac", type=float, default=0.625,
+                    help="fraction of output channels in the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-regime section")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-profile", metavar="DIR")
+    args = ap.parse_args()
+
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile)
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this benchmark runs on one GPU only (got --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); multi-GPU scaling is not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+
+    import fp8_dynamic_quantized_amd as F
+    import synth
+    from fp8_dynamic_quantized_amd import build as B
+    if not os.path.exists(B.LIB):
+        B.build()
+    F.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    pre = bench_prefill(F, torch, args.steps, args.warmup)
+    M, K, N = pre["dom_shape"]
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(pre["value"], 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(dt / args.steps * 1e3, 4),
+        "ms_per_step": round(pre["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -186,27 +355,28 @@ def main():
             "workload": "Llama-3.1-8B prefill linears, M=4096 tokens: qkv 4096->6144, "
                         "o 4096->4096, gate_up 4096->28672, down 14336->4096; "
                         "per-token dynamic / per-channel static E4M3, bf16 in/out",
-            "M": M,
-            "shapes": [[L["name"], L["K"], L["N"]] for L in layers],
+            "M": pre["M"],
+            "shapes": pre["shapes"],
             "parallelism": "single GPU",
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_prefill_kernel<256,256> (gate_up 4096x4096->28672)",
-            "achieved": round(achieved, 1),
+            "kernel": f"{DOM_KERNEL} (gate_up {M}x{K} -> {N})",
+            "achieved": round(pre["achieved"], 1),
             "peak": PEAK_FP8_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-            "traffic": None,
+            "frac": round(pre["achieved"] / PEAK_FP8_TFLOPS, 4),
+            "traffic": read_traffic(),
+            "avg_launch_us": round(pre["dom_us"], 2),
         },
-        "per_linear": per_layer,
+        "per_linear": pre["per_layer"],
     }
+    if not args.no_decode:
+        out["decode"] = bench_decode(F, torch)
     if not args.no_cpu_baseline:
-        for L in layers:
-            del L["x"], L["qw"], L["y"], L["qx"]
-        torch.cuda.empty_cache()
         log("cpu baseline (oracle) ...")
-        out["cpu_baseline"] = cpu_baseline(shapes, M, args.cpu_rows, args.cpu_col_frac)
+        out["cpu_baseline"] = cpu_baseline(synth.SHAPES["c2"], args.cpu_rows,
+                                           args.cpu_col_frac)
     print(json.dumps(out), flush=True)
 
 
