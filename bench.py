@@ -217,7 +217,7 @@ def bench_decode(F, torch, batches=7, per_batch=20, warm=5):
             qx = torch.empty((M, K), dtype=torch.uint8, device="cuda")
             sx = torch.empty((M,), dtype=torch.float32, device="cuda")
             need = F.fp8_workspace_bytes(M, N, K)
-            ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+            ws = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
             c = [0]
 
             def run():

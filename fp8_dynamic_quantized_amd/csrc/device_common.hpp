@@ -81,4 +81,25 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
   return v;
 }
 
+
+// LDS (address space 3) pointer, for taking the 32-bit LDS address of a
+// shared array.
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// One global_load_lds_dwordx4: 16 bytes from base + off (off per lane, base
+// wave-uniform) to LDS byte address lds + 16 * lane (lds wave-uniform). It
+// has no result registers; completion is observed with vmcnt, which callers
+// wait for explicitly (issued from asm so that the compiler adds no waits of
+// its own before LDS reads). M0 carries the LDS base and needs one wait
+// state before the load reads it.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory", "m0");
+}
+
 }  // namespace fp8dq

@@ -249,15 +249,24 @@ DecodePlan plan_decode(int64_t M, int64_t N, int64_t K) {
 #ifdef FP8DQ_DEC_NB
   p.nb = FP8DQ_DEC_NB;
 #else
-  // Two weight row-blocks per workgroup halve the activation re-reads per
-  // weight byte (worth it from M > 16) and suit very wide layers.
+#ifdef FP8DQ_DEC_NB_WIDE
   p.nb = (M > 16 || N / 32 >= 1024) ? 2 : 1;
+#else
+  // Two weight row-blocks per workgroup halve the activation re-reads per
+  // weight byte, which pays from M > 16; below, single blocks stream better.
+  p.nb = M > 16 ? 2 : 1;
+#endif
+#endif
+#ifdef FP8DQ_DEC_TARGET
+  const int64_t target = FP8DQ_DEC_TARGET;
+#else
+  const int64_t target = 512;
 #endif
   const int64_t wgs = (N + 16 * p.nb - 1) / (16 * p.nb);
-  // Split K across the grid until there are >= 512 workgroups, keeping at
-  // least 8 K steps (2 per wave) in each slice.
+  // Split K across the grid until there are >= target workgroups, keeping
+  // at least 8 K steps (2 per wave) in each slice.
   int64_t splits = 1;
-  while (wgs * splits < 512 && KT / (splits * 2) >= 8) splits *= 2;
+  while (wgs * splits < target && KT / (splits * 2) >= 8) splits *= 2;
   p.kt_per_split = (int)((KT + splits - 1) / splits);
   p.splits = (int)((KT + p.kt_per_split - 1) / p.kt_per_split);
   return p;

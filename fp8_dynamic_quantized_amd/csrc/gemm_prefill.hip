@@ -41,7 +41,6 @@ constexpr int GM = 8;  // tile rows per L2 group
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 constexpr int kVmcnt0 = vmcnt_imm(0);
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(1))) void* gbl_ptr;
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
@@ -272,20 +271,6 @@ __device__ __forceinline__ int dh(int r) {   // chunk permutation of row r
 }
 __device__ __forceinline__ int dlds_off(int row, int c) {
   return (row >> 4) * 1024 + ((dq(row & 15) << 2) + (c ^ dh(row))) * 16;
-}
-
-// One global_load_lds_dwordx4: 16 bytes from base + off (off per lane, base
-// wave-uniform) to LDS byte address lds + 16 * lane (lds wave-uniform). It
-// has no result registers; completion is observed with vmcnt. M0 carries the
-// LDS base and needs one wait state before the load reads it.
-__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(off), "s"(base), "s"(lds)
-      : "memory", "m0");
 }
 
 // BN: tile width (256 or 128); S: ring slots; WPC: workgroups per CU the

@@ -339,6 +339,42 @@ def test_c5_full_size_sampled(F):
 
 
 # ----------------------------------------------------------------------------
+# Decode path (M <= 64): ragged shapes, split-K, the two-step equivalence
+# ----------------------------------------------------------------------------
+DECODE_CASES = [(1, 8192, 8192), (5, 100, 1664), (16, 1024, 4096), (17, 520, 3200),
+                (33, 4096, 896), (64, 10240, 8192), (64, 33, 128), (2, 2048, 28672),
+                (8, 57344, 8192)]
+
+
+@pytest.mark.parametrize("M,N,K", DECODE_CASES)
+def test_decode_linear_shapes(F, M, N, K):
+    """fp8_linear at M <= 64 (the split-K decode path): codes and scales
+    bit-exact, y within tolerance on sampled columns, y bit-identical to
+    fp8_quant_act + fp8_gemm forced onto the decode path, and repeated calls
+    reproduce the result."""
+    say(f"decode {M}x{N}x{K}")
+    xb = synth.activations(M, K, 1200 + M, 1300 + K)
+    wb = synth.weights(N, K, 1400 + N + K)
+    qw_d, sw_d = F.fp8_quant_act(dev_bf16(wb))
+    cols = sample_idx(N, 256, M)
+    qw_o, sw_o = O.quant_per_row(wb[cols])
+    x_d = dev_bf16(xb)
+    y, qx, sx = F.fp8_linear(x_d, qw_d, sw_d)
+    y_again, _, _ = F.fp8_linear(x_d, qw_d, sw_d)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_again.view(torch.int16)), "repeat"
+    qx_o, sx_o = O.quant_per_row(xb)
+    assert_scales_equal(sx.cpu().numpy(), sx_o, "act scales")
+    assert_codes_equal(qx.cpu().numpy(), qx_o, "act codes")
+    cols_d = torch.from_numpy(cols).cuda()
+    assert_y_close(host_bf16_f64(y[:, cols_d]),
+                   O.linear_per_channel(qx_o, sx_o, qw_o, sw_o), "y")
+    y2 = F.fp8_gemm(qx, sx, qw_d, sw_d, flags=F.FORCE_DECODE)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "linear vs two-step"
+
+
+# ----------------------------------------------------------------------------
 # Determinism and guard bands
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("M,N,K,flags", [(4096, 4096, 4096, 0), (16, 1024, 4096, 0),
