@@ -273,10 +273,34 @@ __device__ __forceinline__ int dlds_off(int row, int c) {
   return (row >> 4) * 1024 + ((dq(row & 15) << 2) + (c ^ dh(row))) * 16;
 }
 
+// One global_load_lds_dword: 4 bytes from base + off (off per lane) to LDS
+// byte address lds + 4 * lane (M0 = lds). Completion is observed with vmcnt.
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, %1"
+      :
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory", "m0");
+}
+
 // BN: tile width (256 or 128); S: ring slots; WPC: workgroups per CU the
 // register / LDS budget is sized for (two let one workgroup's MFMAs cover the
 // other's barrier and memory waits).
-template <int BN, int S, int WPC>
+// BLOCK (block variant, S odd): two 64-byte stages make one 128-wide scale
+// group g, whose products count with the factor f_g = sx[m, g] * sw[nb, g]
+// (nb = the wave's 128-row weight block). One accumulator carries the sum
+// in units of the latest factor: before group g's first MFMAs the
+// accumulator of row m is multiplied by f_{g-1} / f_g, and the epilogue
+// multiplies by the last factor, so y = sum_g f_g P_g up to fp32 rounding
+// (one rounding per group; a zero factor -- an all-zero group, whose codes
+// and products are zero -- leaves the accumulator as it is). The
+// activation scales of a group (256 tile rows) come into a 4-slot LDS ring
+// with one 4-byte direct load per wave, issued on even steps two groups
+// ahead (the same explicit wait counts cover them); the workgroup's weight
+// block scales are copied to LDS once.
+template <int BN, int S, int WPC, bool BLOCK>
 __global__ __launch_bounds__(256, WPC) void gemm_prefill_deep_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint8_t* __restrict__ qw, const float* __restrict__ sw,
@@ -288,6 +312,9 @@ __global__ __launch_bounds__(256, WPC) void gemm_prefill_deep_kernel(
   constexpr int DLPS = DXQ + DWQ;                 // loads per wave per stage
   constexpr int STAGE = (BM + BN) * DBK;
   constexpr int XB = BM * DBK;  // W tile offset inside a stage
+  constexpr int RING = S * STAGE;                 // block variant: scale areas follow
+  constexpr int EPI = DTN * 2 + 8;                // LDS row stride of the epilogue staging
+  static_assert(!BLOCK || (S & 1) == 1, "block variant: S odd");
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const int nblk = gridDim.x;
@@ -320,6 +347,21 @@ __global__ __launch_bounds__(256, WPC) void gemm_prefill_deep_kernel(
   }
   const int KT = K / DBK;  // even: K is a multiple of 128
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)smem;
+  const int G = K / 128;                          // scale groups
+  float* sxs = reinterpret_cast<float*>(smem + RING);          // [4][256]
+  float* sws = reinterpret_cast<float*>(smem + RING + 4096);   // [BN/128][G]
+  // activation scales of group g (tile rows 64*wave .. +63) -> slot g & 3
+  const uint32_t sxoff =
+      (uint32_t)min(m0 + 64 * wave + lane, M - 1) * (uint32_t)G * 4u;
+  auto issue_sx = [&](int g) {
+    g = min(max(g, 0), G - 1);
+    dma4(sx, sxoff + (uint32_t)g * 4u,
+         lds0 + (uint32_t)(RING + (g & 3) * 1024 + 256 * wave));
+  };
+  if constexpr (BLOCK) {  // the tile's BN/128 weight blocks (N % 128 == 0)
+    const float* swr = sw + (int64_t)(n0 / 128) * G;
+    for (int g = tid; g < (BN / 128) * G; g += 256) sws[g] = swr[g];  // published by the prologue barrier
+  }
   // Load q (0 .. DLPS-1) of K step min(kt, KT-1) into ring slot kt % S. Past
   // the end the last step is loaded again into a slot that is never read,
   // which keeps the number of loads in flight (and so every wait count)
@@ -345,12 +387,22 @@ __global__ __launch_bounds__(256, WPC) void gemm_prefill_deep_kernel(
     for (int j = 0; j < DMJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  // prologue: steps 0 .. S-2 in flight; step 0 published and read
+  float fcur[DMJ];  // block variant: factor the accumulator is counted in
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s)
+  for (int j = 0; j < DMJ; ++j) fcur[j] = 0.f;
+
+  // prologue: steps 0 .. S-2 in flight; step 0 published and read. In the
+  // block variant, the load issues of the prologue's steps stand for issue
+  // steps -(S-1) .. -1; the even ones carry a scale load too (group 0), so
+  // that every steady-state wait count below holds from the first step.
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) {
+    if constexpr (BLOCK) {  // virtual even issue steps -4, -2: groups 0, 1
+      if (((s - (S - 1)) & 1) == 0) issue_sx((s - (S - 1)) / 2 + 2);
+    }
 #pragma unroll
     for (int q = 0; q < DLPS; ++q) issue_one(s, q);
+  }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * DLPS));
   __syncthreads();
   v8i A[2][DNI], B[2][DMJ];
@@ -373,27 +425,58 @@ __global__ __launch_bounds__(256, WPC) void gemm_prefill_deep_kernel(
   // the LDS latency of every read hides under the MFMAs of the current step.
   constexpr int NM = DNI * DMJ;          // MFMAs per step
   constexpr int NR = 2 * (DNI + DMJ);    // fragment halves per step
-  static_assert(NR <= NM && DLPS <= NM, "one read / load per MFMA at most");
+  constexpr int RPM = (NR + NM - 1) / NM;  // fragment reads per MFMA slot
+  static_assert(RPM <= 2 && DLPS <= NM, "at most two reads / one load per MFMA");
+  // loads issued after step kt+1's: S-3 steps, plus (block) one scale load
+  // for every even step among them
+  constexpr int WAITN = (S - 3) * DLPS + (BLOCK ? (S - 3) / 2 : 0);
+  // block variant: factor of group g for this lane's rows, and the rescale
+  // of the accumulator from the previous factor to it
+  auto group_rescale = [&](int g, float (&rho)[DMJ]) {
+    const float* sl = sxs + (g & 3) * 256 + wm * DTM + lr;
+    const float swg = sws[wn * (DTN / 128) * G + g];
+#pragma unroll
+    for (int j = 0; j < DMJ; ++j) {
+      const float f = sl[32 * j] * swg;
+      const bool live = f != 0.0f;
+      rho[j] = live ? fcur[j] / f : 1.0f;
+      fcur[j] = live ? f : fcur[j];
+    }
+  };
   auto step = [&](int kt, auto cur_c, auto more_c) {
     constexpr int cur = decltype(cur_c)::value;
     constexpr bool more = decltype(more_c)::value;
     if (more) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 3) * DLPS));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(WAITN));
       __syncthreads();
     }
     const uint8_t* nX = smem + ((kt + 1) % S) * STAGE;
     const uint8_t* nW = nX + XB;
+    // block variant, first stage of group g = kt/2: rescale to f_g
+    float rho[DMJ];
+    if constexpr (BLOCK && cur == 0) {
+      group_rescale(kt / 2, rho);
+      if (more) issue_sx(kt / 2 + 2);   // two groups ahead of its first stage
+    }
 #pragma unroll
     for (int t = 0; t < NM; ++t) {
       if (more) {
-        if (t < NR) {
-          const int f = t >> 1, h = t & 1;
-          if (f < DNI) rd_half(A[cur ^ 1][f], nW, arow0 + 32 * f, h);
-          else rd_half(B[cur ^ 1][f - DNI], nX, brow0 + 32 * (f - DNI), h);
+#pragma unroll
+        for (int u = 0; u < RPM; ++u) {
+          const int r = t * RPM + u;
+          if (r < NR) {
+            const int f = r >> 1, h = r & 1;
+            if (f < DNI) rd_half(A[cur ^ 1][f], nW, arow0 + 32 * f, h);
+            else rd_half(B[cur ^ 1][f - DNI], nX, brow0 + 32 * (f - DNI), h);
+          }
         }
         if (t < DLPS) issue_one(kt + S - 1, t);
       }
       const int i = t / DMJ, j = t % DMJ;
+      if constexpr (BLOCK && cur == 0) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] *= rho[j];
+      }
       acc[i][j] = mfma_e4m3_32x32x64(A[cur][i], B[cur][j], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -415,40 +498,47 @@ __global__ __launch_bounds__(256, WPC) void gemm_prefill_deep_kernel(
   // banks), then stores it row-wise, 16 bytes per lane: every store
   // instruction covers whole 256-byte row segments.
   __syncthreads();  // every wave is done reading the ring
-  uint8_t* ep = smem + wave * (DTM * DEPI);
+  uint8_t* ep = smem + wave * (DTM * EPI);
 #pragma unroll
   for (int j = 0; j < DMJ; ++j) {
     const int ml = 32 * j + lr;
-    const float sm = sx[min(m0 + wm * DTM + ml, M - 1)];
+    const float sm = BLOCK ? fcur[j] : sx[min(m0 + wm * DTM + ml, M - 1)];
 #pragma unroll
     for (int i = 0; i < DNI; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int nl = 32 * i + 8 * q + 4 * kh;
         const int n = n0 + wn * DTN + nl;
-        float s4[4];
-        if (n + 3 < N) {
-          const float4 t = *reinterpret_cast<const float4*>(sw + n);
-          s4[0] = t.x; s4[1] = t.y; s4[2] = t.z; s4[3] = t.w;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) s4[r] = (n + r < N) ? sw[n + r] : 0.f;
-        }
         uint2 pk;
-        pk.x = pack_bf16x2(acc[i][j][4 * q + 0] * sm * s4[0], acc[i][j][4 * q + 1] * sm * s4[1]);
-        pk.y = pack_bf16x2(acc[i][j][4 * q + 2] * sm * s4[2], acc[i][j][4 * q + 3] * sm * s4[3]);
-        *reinterpret_cast<uint2*>(ep + ml * DEPI + nl * 2) = pk;
+        if constexpr (BLOCK) {  // sum counted in units of the last factor
+          pk.x = pack_bf16x2(acc[i][j][4 * q + 0] * sm, acc[i][j][4 * q + 1] * sm);
+          pk.y = pack_bf16x2(acc[i][j][4 * q + 2] * sm, acc[i][j][4 * q + 3] * sm);
+        } else {
+          float s4[4];
+          if (n + 3 < N) {
+            const float4 t = *reinterpret_cast<const float4*>(sw + n);
+            s4[0] = t.x; s4[1] = t.y; s4[2] = t.z; s4[3] = t.w;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s4[r] = (n + r < N) ? sw[n + r] : 0.f;
+          }
+          pk.x = pack_bf16x2(acc[i][j][4 * q + 0] * sm * s4[0], acc[i][j][4 * q + 1] * sm * s4[1]);
+          pk.y = pack_bf16x2(acc[i][j][4 * q + 2] * sm * s4[2], acc[i][j][4 * q + 3] * sm * s4[3]);
+        }
+        *reinterpret_cast<uint2*>(ep + ml * EPI + nl * 2) = pk;
       }
     }
   }
-  const int rsub = lane >> 4, cseg = lane & 15;  // 4 rows x 16 segments of 16 B
+  constexpr int SEGS = DTN / 8;                  // 16-byte segments per row
+  constexpr int RPI = 64 / SEGS;                 // rows per store instruction
+  const int rsub = lane / SEGS, cseg = lane % SEGS;
   const int nbase = n0 + wn * DTN + 8 * cseg;
   const bool vec_ok = (N & 7) == 0 && nbase + 7 < N;
 #pragma unroll 4
-  for (int t = 0; t < DTM / 4; ++t) {
-    const int ml = 4 * t + rsub;
+  for (int t = 0; t < DTM / RPI; ++t) {
+    const int ml = RPI * t + rsub;
     const int m = m0 + wm * DTM + ml;
-    const uint8_t* src = ep + ml * DEPI + cseg * 16;
+    const uint8_t* src = ep + ml * EPI + cseg * 16;
     const uint2 lo = *reinterpret_cast<const uint2*>(src);
     const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
     if (m < M) {
@@ -465,25 +555,29 @@ __global__ __launch_bounds__(256, WPC) void gemm_prefill_deep_kernel(
   }
 }
 
-template <int BN, int S, int WPC>
+template <int BN, int S, int WPC, bool BLOCK = false>
 void launch_deep(const uint8_t* qx, const float* sx, const uint8_t* qw,
                  const float* sw, void* y, int64_t M, int64_t N, int64_t K,
                  hipStream_t st) {
   constexpr int ring = S * (256 + BN) * DBK;
-  constexpr int stage_out = 4 * 128 * DEPI;  // epilogue staging, 4 waves
-  constexpr int smem = ring > stage_out ? ring : stage_out;
-  static_assert(smem * WPC <= 160 * 1024, "LDS budget");
+  constexpr int stage_out = 4 * 128 * (BN + 8);  // epilogue staging, 4 waves
+  constexpr int smem_max = (BLOCK ? ring + 4096 + 4 * 1024 * (BN / 128) : ring);
+  constexpr int smem_cap = smem_max > stage_out ? smem_max : stage_out;
+  static_assert(smem_cap * WPC <= 160 * 1024, "LDS budget");
+  // block variant: + activation-scale ring (4 KB) + the weight block scales
+  const int smem_need = BLOCK ? ring + 4096 + (int)((K / 128) * 4 * (BN / 128)) : ring;
+  const int smem = smem_need > stage_out ? smem_need : stage_out;
   static std::once_flag once;
   std::call_once(once, [] {
     (void)hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_prefill_deep_kernel<BN, S, WPC>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+        reinterpret_cast<const void*>(&gemm_prefill_deep_kernel<BN, S, WPC, BLOCK>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, smem_cap);
   });
   const int tiles_m = (int)((M + 255) / 256);
   const int tiles_n = (int)((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_prefill_deep_kernel<BN, S, WPC>), dim3((unsigned)(tiles_m * tiles_n)),
-                     dim3(256), smem, st, qx, sx, qw, sw, (uint16_t*)y, (int)M,
-                     (int)N, (int)K, tiles_m, tiles_n);
+  hipLaunchKernelGGL((gemm_prefill_deep_kernel<BN, S, WPC, BLOCK>),
+                     dim3((unsigned)(tiles_m * tiles_n)), dim3(256), smem, st, qx, sx, qw,
+                     sw, (uint16_t*)y, (int)M, (int)N, (int)K, tiles_m, tiles_n);
 }
 
 template <int BM, int BN, bool BLOCK>
@@ -521,7 +615,17 @@ void launch_gemm_prefill(const uint8_t* qx, const float* sx, const uint8_t* qw,
   const bool use_big = big >= 256;
 #endif
   if (block) {
-    if (use_big) launch_cfg<256, 256, true>(qx, sx, qw, sw, y, M, N, K, st);
+    // deep kernel: 32-bit scale offsets and at most 1024 scale groups
+    const bool deep_ok = K <= 131072 && (uint64_t)M * (uint64_t)(K / 128) * 4u < (1ull << 32);
+#if defined(FP8DQ_BLOCK_OLD)
+    const bool deep = false;
+#else
+    const bool deep = deep_ok;
+#endif
+    if (deep) {
+      launch_deep<128, 5, 1, true>(qx, sx, qw, sw, y, M, N, K, st);
+    }
+    else if (use_big) launch_cfg<256, 256, true>(qx, sx, qw, sw, y, M, N, K, st);
     else launch_cfg<256, 128, true>(qx, sx, qw, sw, y, M, N, K, st);
   } else {
 #if defined(FP8DQ_TILE_OVERRIDE) && FP8DQ_TILE_OVERRIDE == 3
