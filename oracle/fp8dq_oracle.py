@@ -267,3 +267,196 @@ def within_tolerance(y_gpu, y_ref, rtol: float = 1e-2, atol: float = 1e-3):
     y_gpu = np.asarray(y_gpu, np.float64)
     y_ref = np.asarray(y_ref, np.float64)
     return np.abs(y_gpu - y_ref) <= atol + rtol * np.abs(y_ref)
+
+
+# ----------------------------------------------------------------------------
+# Producers of the quantizer's input, fused with it downstream ("next" rows).
+# Each is defined as its exact real-valued formula, evaluated in float64 and
+# rounded once to bfloat16 (the model's activation dtype); the FP8 per-token
+# quantization then applies to that bf16 tensor exactly as above.
+# ----------------------------------------------------------------------------
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+RMS_EPS = 1e-5   # RMSNorm epsilon ("Llama 3 精读实录" page, §1.3)
+
+
+def f64_to_bf16_bits(y: np.ndarray) -> np.ndarray:
+    """float64 -> bfloat16 bit pattern: round to nearest, ties to even, sign
+    of zero kept, magnitudes that round past the largest finite bf16 -> inf."""
+    y = np.asarray(y, dtype=np.float64)
+    r = f64_to_bf16_rne(y)
+    r = np.where(np.abs(r) > BF16_MAX, np.copysign(np.inf, y), r)
+    r = np.copysign(r, y)                      # keep the sign of zero
+    return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _near_bf16_midpoint(h: np.ndarray, rel: float = 2.0 ** -30) -> np.ndarray:
+    """True where a float64 value lies within ``rel`` (relative) of a bf16
+    rounding midpoint -- there the float64 evaluation error could decide the
+    rounding, so the exact value has to."""
+    h = np.asarray(h, np.float64)
+    m, e = np.frexp(h)
+    e = np.maximum(e, -125)
+    scaled = np.ldexp(h, 8 - e)                # bf16 ulps above the point
+    frac = np.abs(scaled - np.floor(scaled) - 0.5)
+    return np.isfinite(h) & (h != 0) & (frac < rel * 256)
+
+
+def _exact_round_bf16(value) -> int:
+    """Exact round-to-nearest-even of a Decimal / Fraction to bf16 bits."""
+    from fractions import Fraction
+    q = Fraction(value)
+    sign = 0x8000 if q < 0 else 0
+    a = abs(q)
+    if a == 0:
+        return sign
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)
+    ulp = Fraction(2) ** (e - 7)
+    n = a / ulp
+    k = n.numerator // n.denominator
+    rem = n - k
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and (k & 1)):
+        k += 1
+    val = k * ulp
+    if val >= Fraction(2) ** 128:
+        return sign | 0x7F80
+    return sign | (int(np.float32(float(val)).view(np.uint32)) >> 16) & 0x7FFF
+
+
+def silu_mul_bf16(gu_bits: np.ndarray) -> np.ndarray:
+    """SwiGLU's gated product h = bf16(silu(g) * u), silu(g) = g / (1 + e^-g).
+
+    g is the first half of the columns of ``gu_bits`` [R, 2I] and u the
+    second half: the gate and up branches of one fused gate_up GEMM, which
+    the "Llama 3 精读实录" page (§1.3) says are computed separately and then
+    multiplied elementwise. Returns bf16 bits [R, I].
+
+    Evaluated in float64. Where the float64 value lies within 2^-30 of the
+    midpoint m between two bf16 neighbours, the side of m is decided exactly
+    (for g > 37 float64 rounds silu(g) to g and can turn h into an exact tie
+    that the true value misses): with s = 1 / (1 + e^-g) > 0,
+        h - m = s * ((g*u - m) - m * e^-g),
+    where g*u - m is an exact rational and m * e^-g is taken to 60 digits.
+    """
+    from decimal import Decimal, localcontext
+    from fractions import Fraction
+    gu = bf16_to_f64(gu_bits)
+    half = gu.shape[1] // 2
+    g, u = gu[:, :half], gu[:, half:]
+    with np.errstate(over="ignore"):
+        sil = g / (1.0 + np.exp(-g))           # e^-g = inf -> silu = -0
+    h = sil * u
+    out = f64_to_bf16_bits(h)
+    for r, c in zip(*np.nonzero(_near_bf16_midpoint(h))):
+        gv, uv, hv = float(g[r, c]), float(u[r, c]), float(h[r, c])
+        # the two bf16 neighbours of hv and their midpoint
+        lo_bits = int(np.float32(hv).view(np.uint32)) >> 16     # truncation (|.| down)
+        lo = float(np.uint32(lo_bits << 16).view(np.float32))
+        hi = float(np.uint32((lo_bits + 1) << 16).view(np.float32))
+        m = (Fraction(lo) + Fraction(hi)) / 2
+        a = Fraction(gv) * Fraction(uv) - m
+        with localcontext() as ctx:
+            ctx.prec = 60
+            try:
+                b = Fraction(Decimal(m.numerator) / Decimal(m.denominator) * Decimal(-gv).exp())
+            except ArithmeticError:   # e^-g beyond any decimal exponent: g < 0 huge
+                b = None
+        if b is None:
+            side = -1 if hv > 0 else 1   # unreachable for near-midpoint values
+        else:
+            d = a - b
+            side = (d > 0) - (d < 0)     # sign of h - m
+        up = side * (1 if hv > 0 else -1)            # sign of |h| - |m|
+        if up > 0 or (up == 0 and (lo_bits & 1)):
+            out[r, c] = lo_bits + 1
+        else:
+            out[r, c] = lo_bits
+    return out
+
+
+def silu_mul_quant(gu_bits: np.ndarray):
+    """Per-token FP8 quantization of h = silu_mul_bf16(gu). (codes, scales)."""
+    return quant_per_row(silu_mul_bf16(gu_bits))
+
+
+def rmsnorm_bf16(x_bits: np.ndarray, gamma_bits: np.ndarray,
+                 eps: float = RMS_EPS) -> np.ndarray:
+    """RMSNorm h = bf16(gamma * x / sqrt(mean(x^2) + eps)) per row of x [R, H].
+
+    eps = 1e-5 and the norm before attention and the MLP ("Llama 3 精读实录"
+    page, §1.3); the page keeps RMSNorm itself in bf16 (§5.3), so its output
+    is the bf16 tensor that the FP8 quantization then reads. Evaluated in
+    float64; elements within 2^-30 of a bf16 rounding midpoint are evaluated
+    again exactly (rational mean square, 60-digit square root).
+    """
+    from decimal import Decimal, localcontext
+    from fractions import Fraction
+    x = bf16_to_f64(x_bits)
+    gam = bf16_to_f64(gamma_bits)[None, :]
+    ms = np.mean(x * x, axis=1, keepdims=True)
+    h = gam * x / np.sqrt(ms + eps)
+    out = f64_to_bf16_bits(h)
+    near = _near_bf16_midpoint(h)
+    for r in np.unique(np.nonzero(near)[0]):   # exact evaluation near midpoints
+        with localcontext() as ctx:
+            ctx.prec = 60
+            q = sum(Fraction(float(v)) ** 2 for v in x[r]) / x.shape[1] + Fraction(eps)
+            rinv = 1 / (Decimal(q.numerator) / Decimal(q.denominator)).sqrt()
+            for c in np.nonzero(near[r])[0]:
+                out[r, c] = _exact_round_bf16(Decimal(float(gam[0, c])) *
+                                              Decimal(float(x[r, c])) * rinv)
+    return out
+
+
+def rmsnorm_quant(x_bits, gamma_bits, eps: float = RMS_EPS):
+    """Per-token FP8 quantization of rmsnorm_bf16(x, gamma). (codes, scales)."""
+    return quant_per_row(rmsnorm_bf16(x_bits, gamma_bits, eps))
+
+
+def nearest_rank(n: int, permille: int) -> int:
+    """1-based rank of the permille/1000 quantile of n values, nearest-rank
+    method: ceil(p * n), kept inside [1, n]. Exact integer arithmetic."""
+    k = -((-permille * n) // 1000)
+    return int(min(max(k, 1), n))
+
+
+def calib_amax(x_bits: np.ndarray, lo_permille: int = 1, hi_permille: int = 999) -> float:
+    """Static calibration range of a tensor: the larger magnitude of its
+    lo- and hi-quantiles (P0.1 and P99.9 by default), instead of max |x| --
+    the "Llama 3 精读实录" page, §2.2 (percentiles as the dynamic range)."""
+    v = np.sort(bf16_to_f64(x_bits).ravel())
+    n = v.size
+    if n == 0:
+        return 0.0
+    lo = v[nearest_rank(n, lo_permille) - 1]
+    hi = v[nearest_rank(n, hi_permille) - 1]
+    return float(max(abs(lo), abs(hi)))
+
+
+def calib_scale(x_bits, lo_permille: int = 1, hi_permille: int = 999) -> np.float32:
+    """fp32 static per-tensor scale RN(calib_amax / 448)."""
+    return scale_from_amax(np.array([calib_amax(x_bits, lo_permille, hi_permille)]))[0]
+
+
+def quant_static(x_bits: np.ndarray, s) -> np.ndarray:
+    """E4M3 codes of x / s with one fixed (static) fp32 scale for the whole
+    tensor. Values beyond 448 * s saturate to +-448 (codes 0x7E / 0xFE)."""
+    return quantize_with_scale(bf16_to_f64(x_bits), np.float32(s))
+
+
+def kv_quant_scatter(k_bits: np.ndarray, v_bits: np.ndarray, slots: np.ndarray):
+    """FP8 KV cache write ("Llama 3 精读实录" page, §4.1: FP8 also compresses
+    the KV cache): each token row of K and V [T, width] is quantized per
+    token and lands in cache row slots[t] (negative: not written).
+
+    Returns {slot: (k_codes, k_scale, v_codes, v_scale)} for the written rows.
+    """
+    qk, sk = quant_per_row(k_bits)
+    qv, sv = quant_per_row(v_bits)
+    out = {}
+    for t, slot in enumerate(np.asarray(slots).tolist()):
+        if slot >= 0:
+            out[int(slot)] = (qk[t], sk[t], qv[t], sv[t])
+    return out
