@@ -34,6 +34,15 @@ _SIGS = {
     "fp8_linear_block": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _c_p,
                                         _c_p, ctypes.c_uint32, _c_p, ctypes.c_size_t, _c_p]),
     "fp8_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, ctypes.c_int32, ctypes.c_uint32]),
+    "fp8_silu_mul_quant": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p]),
+    "fp8_rmsnorm_quant": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, ctypes.c_double, _c_p,
+                                         _c_p, _c_p]),
+    "fp8_calib_workspace_bytes": (ctypes.c_size_t, [_i64]),
+    "fp8_calib_scale": (ctypes.c_int, [_c_p, _i64, ctypes.c_int32, ctypes.c_int32, _c_p,
+                                       _c_p, ctypes.c_size_t, _c_p]),
+    "fp8_quant_static": (ctypes.c_int, [_c_p, _i64, _c_p, _c_p, _c_p]),
+    "fp8_kv_cache_quant": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, _c_p, _i64, _c_p, _c_p,
+                                          _c_p, _c_p, _c_p]),
     "fp8_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fp8dq_version": (ctypes.c_char_p, []),
 }
@@ -213,3 +222,92 @@ def fp8_linear_block(x, qw, sw, y=None, qx_out=None, sx_out=None,
         _ptr(x), _ptr(qw), _ptr(sw), _ptr(y), M, N, K, _ptr(qx_out), _ptr(sx_out),
         flags, _ptr(ws), nb, _stream(x, stream)))
     return y, qx_out, sx_out
+
+
+# ----------------------------------------------------------------------------
+# Fused producers, static calibration, FP8 KV cache
+# ----------------------------------------------------------------------------
+RMS_EPS = 1e-5
+
+
+def fp8_silu_mul_quant(gu, q=None, scale=None, stream=None):
+    """gu bf16 [rows, 2I] = (gate | up) -> per-token FP8 of bf16(silu(gate) * up).
+
+    Returns (codes uint8 [rows, I], scales fp32 [rows])."""
+    import torch
+    rows, two_i = gu.shape
+    _need(gu, torch.bfloat16, (rows, two_i), "gu")
+    if two_i % 2:
+        raise ValueError("gu: the column count must be even (gate | up)")
+    inner = two_i // 2
+    q = torch.empty((rows, inner), dtype=torch.uint8, device=gu.device) if q is None else q
+    scale = torch.empty((rows,), dtype=torch.float32, device=gu.device) if scale is None else scale
+    _check("fp8_silu_mul_quant", lib().fp8_silu_mul_quant(
+        _ptr(gu), rows, inner, _ptr(q), _ptr(scale), _stream(gu, stream)))
+    return q, scale
+
+
+def fp8_rmsnorm_quant(x, gamma, eps: float = RMS_EPS, q=None, scale=None, stream=None):
+    """x bf16 [rows, H], gamma bf16 [H] -> per-token FP8 of
+    bf16(gamma * x / sqrt(mean(x^2) + eps)). Returns (codes, scales)."""
+    import torch
+    rows, hidden = x.shape
+    _need(x, torch.bfloat16, (rows, hidden), "x")
+    _need(gamma, torch.bfloat16, (hidden,), "gamma")
+    q = torch.empty((rows, hidden), dtype=torch.uint8, device=x.device) if q is None else q
+    scale = torch.empty((rows,), dtype=torch.float32, device=x.device) if scale is None else scale
+    _check("fp8_rmsnorm_quant", lib().fp8_rmsnorm_quant(
+        _ptr(x), _ptr(gamma), rows, hidden, float(eps), _ptr(q), _ptr(scale),
+        _stream(x, stream)))
+    return q, scale
+
+
+def fp8_calib_workspace_bytes(n: int) -> int:
+    return int(lib().fp8_calib_workspace_bytes(n))
+
+
+def fp8_calib_scale(x, lo_permille: int = 1, hi_permille: int = 999, scale=None,
+                    ws=None, stream=None):
+    """Static per-tensor scale RN(max(|P_lo|, |P_hi|) / 448) of a bf16 tensor
+    (nearest-rank percentiles, per mille). Returns a device fp32 [1] tensor."""
+    import torch
+    if x.dtype != torch.bfloat16 or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("x: contiguous bf16 device tensor expected")
+    n = x.numel()
+    scale = torch.empty((1,), dtype=torch.float32, device=x.device) if scale is None else scale
+    need = fp8_calib_workspace_bytes(n)
+    ws = torch.empty(need, dtype=torch.uint8, device=x.device) if ws is None else ws
+    _check("fp8_calib_scale", lib().fp8_calib_scale(
+        _ptr(x), n, lo_permille, hi_permille, _ptr(scale), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(x, stream)))
+    return scale
+
+
+def fp8_quant_static(x, scale, q=None, stream=None):
+    """E4M3 codes of a bf16 tensor with one static device-resident fp32 scale
+    (saturating at +-448). Returns codes with x's shape."""
+    import torch
+    if x.dtype != torch.bfloat16 or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("x: contiguous bf16 device tensor expected")
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if q is None else q
+    _check("fp8_quant_static", lib().fp8_quant_static(
+        _ptr(x), x.numel(), _ptr(scale), _ptr(q), _stream(x, stream)))
+    return q
+
+
+def fp8_kv_cache_quant(k, v, slots, k_cache, v_cache, k_scale, v_scale, stream=None):
+    """Per-token FP8 quantization of K and V [T, width] (bf16) into cache rows
+    slots[t] (int64; negative or >= the cache's rows: not written)."""
+    import torch
+    T, width = k.shape
+    _need(k, torch.bfloat16, (T, width), "k")
+    _need(v, torch.bfloat16, (T, width), "v")
+    _need(slots, torch.int64, (T,), "slots")
+    n_slots = k_cache.shape[0]
+    _need(k_cache, torch.uint8, (n_slots, width), "k_cache")
+    _need(v_cache, torch.uint8, (n_slots, width), "v_cache")
+    _need(k_scale, torch.float32, (n_slots,), "k_scale")
+    _need(v_scale, torch.float32, (n_slots,), "v_scale")
+    _check("fp8_kv_cache_quant", lib().fp8_kv_cache_quant(
+        _ptr(k), _ptr(v), T, width, _ptr(slots), n_slots, _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale), _ptr(v_scale), _stream(k, stream)))

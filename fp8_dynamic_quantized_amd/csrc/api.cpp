@@ -165,6 +165,93 @@ int fp8_linear_block(const void* x_bf16, const uint8_t* qw, const float* sw,
                        ws, ws_bytes, stream, true);
 }
 
+// ---- fused producers, static calibration, KV cache ------------------------
+static constexpr int64_t kMaxFusedRow = 65536;  // values per row of the row kernels
+
+int fp8_silu_mul_quant(const void* gu_bf16, int64_t rows, int64_t I, uint8_t* q,
+                       float* scale, void* stream) {
+  if (rows < 0 || I <= 0 || (I % 8) != 0 || I > kMaxFusedRow) return FP8DQ_ERR_SHAPE;
+  if (rows > INT32_MAX) return FP8DQ_ERR_SHAPE;
+  if (rows == 0) return FP8DQ_OK;
+  if (!gu_bf16 || !q || !scale) return FP8DQ_ERR_NULL;
+  if (!aligned16(gu_bf16) || !aligned16(q) || !aligned16(scale)) return FP8DQ_ERR_ALIGN;
+  if (fp8dq::launch_silu_mul_quant(gu_bf16, rows, I, q, scale, as_stream(stream)) != 0)
+    return FP8DQ_ERR_SHAPE;
+  return launch_status();
+}
+
+int fp8_rmsnorm_quant(const void* x_bf16, const void* gamma_bf16, int64_t rows, int64_t H,
+                      double eps, uint8_t* q, float* scale, void* stream) {
+  if (rows < 0 || H <= 0 || (H % 8) != 0 || H > kMaxFusedRow) return FP8DQ_ERR_SHAPE;
+  if (rows > INT32_MAX) return FP8DQ_ERR_SHAPE;
+  if (!(eps >= 0.0) || eps > 1.0e30) return FP8DQ_ERR_SHAPE;  // NaN fails too
+  if (rows == 0) return FP8DQ_OK;
+  if (!x_bf16 || !gamma_bf16 || !q || !scale) return FP8DQ_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(gamma_bf16) || !aligned16(q) || !aligned16(scale))
+    return FP8DQ_ERR_ALIGN;
+  if (fp8dq::launch_rmsnorm_quant(x_bf16, gamma_bf16, rows, H, eps, q, scale,
+                                  as_stream(stream)) != 0)
+    return FP8DQ_ERR_SHAPE;
+  return launch_status();
+}
+
+size_t fp8_calib_workspace_bytes(int64_t n) {
+  return n < 0 ? 0 : fp8dq::calib_workspace_bytes();
+}
+
+int fp8_calib_scale(const void* x_bf16, int64_t n, int32_t lo_permille, int32_t hi_permille,
+                    float* scale_out, void* ws, size_t ws_bytes, void* stream) {
+  if (n < 0 || (n % 8) != 0 || n >= (int64_t(1) << 32)) return FP8DQ_ERR_SHAPE;
+  if (lo_permille < 0 || hi_permille > 1000 || lo_permille > hi_permille)
+    return FP8DQ_ERR_SHAPE;
+  if ((n > 0 && !x_bf16) || !scale_out || !ws) return FP8DQ_ERR_NULL;
+  if ((n > 0 && !aligned16(x_bf16)) || !aligned16(ws)) return FP8DQ_ERR_ALIGN;
+  if (ws_bytes < fp8dq::calib_workspace_bytes()) return FP8DQ_ERR_WORKSPACE;
+  // nearest-rank order statistics: k = ceil(p * n), kept in [1, n]
+  auto rank = [n](int64_t pm) {
+    int64_t k = (pm * n + 999) / 1000;
+    if (k < 1) k = 1;
+    if (k > n) k = n;
+    return n == 0 ? int64_t(0) : k;
+  };
+  fp8dq::launch_calib_scale(x_bf16, n, rank(lo_permille), rank(hi_permille), scale_out, ws,
+                            as_stream(stream));
+  return launch_status();
+}
+
+int fp8_quant_static(const void* x_bf16, int64_t n, const float* scale, uint8_t* q,
+                     void* stream) {
+  if (n < 0 || (n % 8) != 0) return FP8DQ_ERR_SHAPE;
+  if (n == 0) return FP8DQ_OK;
+  if (!x_bf16 || !scale || !q) return FP8DQ_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(q) || (reinterpret_cast<uintptr_t>(scale) & 3u))
+    return FP8DQ_ERR_ALIGN;
+  fp8dq::launch_quant_static(x_bf16, n, scale, q, as_stream(stream));
+  return launch_status();
+}
+
+int fp8_kv_cache_quant(const void* k_bf16, const void* v_bf16, int64_t T, int64_t width,
+                       const int64_t* slots, int64_t n_slots, uint8_t* k_cache,
+                       uint8_t* v_cache, float* k_scale, float* v_scale, void* stream) {
+  if (T < 0 || width <= 0 || (width % 8) != 0 || width > kMaxFusedRow || n_slots < 0)
+    return FP8DQ_ERR_SHAPE;
+  if (T > INT32_MAX) return FP8DQ_ERR_SHAPE;
+  if (T == 0) return FP8DQ_OK;
+  if (!k_bf16 || !v_bf16 || !slots || !k_cache || !v_cache || !k_scale || !v_scale)
+    return FP8DQ_ERR_NULL;
+  if (!aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || (reinterpret_cast<uintptr_t>(slots) & 7u) ||
+      (reinterpret_cast<uintptr_t>(k_scale) & 3u) || (reinterpret_cast<uintptr_t>(v_scale) & 3u))
+    return FP8DQ_ERR_ALIGN;
+  hipStream_t st = as_stream(stream);
+  if (fp8dq::launch_kv_quant(k_bf16, T, width, slots, n_slots, k_cache, k_scale, st) != 0)
+    return FP8DQ_ERR_SHAPE;
+  int s = launch_status();
+  if (s != FP8DQ_OK) return s;
+  fp8dq::launch_kv_quant(v_bf16, T, width, slots, n_slots, v_cache, v_scale, st);
+  return launch_status();
+}
+
 size_t fp8_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t block,
                            uint32_t flags) {
   if (!known_flags(flags)) return 0;

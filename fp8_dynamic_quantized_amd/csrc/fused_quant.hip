@@ -1,0 +1,509 @@
+// Producers fused with the dynamic FP8 quantizer, static calibration and the
+// FP8 KV-cache write (gfx950).
+//
+// What is computed ("Llama 3 精读实录" page):
+//  * SwiGLU product, §1.3 (gate and up computed separately, then multiplied
+//    elementwise): h = bf16(silu(g) * u), silu(g) = g / (1 + e^-g), g and u
+//    the two halves of the fused gate_up output row; then per-token FP8.
+//  * RMSNorm, §1.3 (eps 1e-5, before attention and the MLP; kept in bf16,
+//    §5.3): h = bf16(gamma * x / sqrt(mean(x^2) + eps)); then per-token FP8.
+//  * Static calibration, §2.2 (P99.9 / P0.1 percentiles as the dynamic
+//    range instead of max): amax = max(|x_(k_lo)|, |x_(k_hi)|) over the
+//    whole tensor (nearest-rank order statistics), s = RN(amax / 448); and
+//    the static quantization x -> E4M3(x / s) with saturation at +-448.
+//  * FP8 KV cache, §4.1: per-token quantization of K and V rows written to
+//    the cache rows a slot mapping names.
+//
+// The bf16 rounding of h is exact (the correctly rounded value of the real
+// formula): h is formed in fp32 with a few ulps of error and rounded to bf16
+// directly unless it lies within 8 fp32 ulps of a bf16 rounding midpoint,
+// is tiny, or (SwiGLU) |g| > 64; those elements are formed again in fp64,
+// where a near-midpoint SwiGLU value is decided by the exact identity
+//   h - m = s * ((g*u - m) - m * e^-g),  s = 1 / (1 + e^-g) > 0,
+// in which g*u - m is exact in fp64. The quantization that follows is the
+// exact codec of the other quantization kernels.
+#include "device_common.hpp"
+#include "kernels.hpp"
+#include "quant_codec.hpp"
+
+namespace fp8dq {
+namespace {
+
+using namespace codec;
+
+constexpr uint32_t kMidTol = 8;  // fp32 ulps around a bf16 rounding midpoint
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits when the value is safely away from a rounding midpoint
+// (the caller has checked); finite or inf.
+__device__ __forceinline__ uint32_t rne16(float h) {
+  const uint32_t b = __float_as_uint(h);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ bool near_mid16(float h) {
+  const uint32_t low = __float_as_uint(h) & 0xFFFFu;
+  return (low - (0x8000u - kMidTol)) <= 2u * kMidTol;
+}
+
+__device__ __forceinline__ bool tiny32(float h) {  // |h| < 2^-100
+  return (__float_as_uint(h) & 0x7FFFFFFFu) < 0x0D800000u;
+}
+
+// Value of bf16 bit pattern b (sign included) as a double; b's magnitude may
+// be one past the largest finite bf16, which stands for 2^128.
+__device__ __forceinline__ double bf16_val(uint32_t b) {
+  if ((b & 0x7FFFu) == 0x7F80u) return (b & 0x8000u) ? -0x1p128 : 0x1p128;
+  return (double)__uint_as_float(b << 16);
+}
+
+// Correctly rounded bf16 of a finite double h (ties to even). Within 2^-30
+// of the midpoint m between h's bf16 neighbours, `tie_side(m, d)` gives the
+// sign of |h| - |m| (d is the fp64 difference |h| - |m|, which a caller
+// without an exact identity returns as is). inf for magnitudes that round
+// past the largest bf16.
+template <typename TieSide>
+__device__ __forceinline__ uint32_t f64_to_bf16(double h, TieSide tie_side) {
+  if (h == 0.0) return (__double_as_longlong(h) < 0) ? 0x8000u : 0u;
+  const float t = __double2float_rz(h);          // truncation toward zero
+  uint32_t lo = __float_as_uint(t) >> 16;        // bf16 neighbour toward zero
+  if ((lo & 0x7FFFu) >= 0x7F80u) return lo & 0xFF80u;  // beyond fp32 range: inf
+  const double m = 0.5 * (bf16_val(lo) + bf16_val(lo + 1));
+  double d = fabs(h) - fabs(m);                  // > 0: round away from zero
+  if (fabs(d) <= 0x1p-30 * fabs(m)) d = tie_side(m, d);
+  if (d > 0.0 || (d == 0.0 && (lo & 1u))) lo += 1;
+  return lo;
+}
+
+// ---- SwiGLU ---------------------------------------------------------------
+__device__ __noinline__ uint32_t silu_mul_slow(float gf, float uf) {
+  const double g = gf, u = uf;
+  const double e = exp(-g);                      // inf for g < -709: h = -0 * u
+  const double h = g / (1.0 + e) * u;
+  return f64_to_bf16(h, [&](double m, double) {
+    // sign(|h| - |m|) = sign(h - m) * sign(m), h - m = s*((g*u - m) - m*e^-g)
+    const double a = fma(g, u, -m);              // exact: g*u has 16 bits
+    const double side = a - m * e;
+    // m * e^-g can underflow (g > 708) while g*u = m exactly: since
+    // silu(g) < g for g > 0, |h| < |g*u| = |m| then.
+    if (side == 0.0) return g > 0.0 ? -1.0 : 0.0;
+    return m > 0.0 ? side : -side;
+  });
+}
+
+__device__ __forceinline__ uint32_t silu_mul1(float g, float u) {
+  if (fabsf(g) <= 64.0f) {
+    const float e = expf(-g);
+    const float h = g / (1.0f + e) * u;
+    if (!near_mid16(h) && !(tiny32(h) && g != 0.0f && u != 0.0f)) return rne16(h);
+  }
+  return silu_mul_slow(g, u);
+}
+
+// 8 gate and 8 up values (one 16-byte chunk each) -> 8 h values (bf16).
+__device__ __forceinline__ uint4 silu_mul8(uint4 gv, uint4 uv) {
+  const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
+  const uint32_t u[4] = {uv.x, uv.y, uv.z, uv.w};
+  uint32_t h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    h[i] = silu_mul1(bf16lo(g[i]), bf16lo(u[i])) |
+           (silu_mul1(bf16hi(g[i]), bf16hi(u[i])) << 16);
+  return make_uint4(h[0], h[1], h[2], h[3]);
+}
+
+// ---- RMSNorm --------------------------------------------------------------
+__device__ __noinline__ uint32_t rms_slow(float xf, float gf, double r) {
+  const double h = (double)xf * r * (double)gf;
+  return f64_to_bf16(h, [](double, double d) { return d; });  // fp64 decides
+}
+
+__device__ __forceinline__ uint32_t rms1(float x, float gm, float r32, double r64) {
+  const float h = x * r32 * gm;
+  if (!near_mid16(h) && !(tiny32(h) && x != 0.0f && gm != 0.0f)) return rne16(h);
+  return rms_slow(x, gm, r64);
+}
+
+__device__ __forceinline__ double chunk_sumsq(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double a = bf16lo(w[i]), b = bf16hi(w[i]);
+    s = fma(a, a, s);
+    s = fma(b, b, s);
+  }
+  return s;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// ---- shared per-row tail: amax of the h chunks, scale, codes ---------------
+template <int CH, int TW>
+__device__ __forceinline__ void quantize_team(const uint4 (&h)[CH], bool row_ok, int64_t row,
+                                              int64_t nch, int team_lane, uint32_t* red,
+                                              uint2* __restrict__ q, float* __restrict__ scale) {
+  constexpr int TEAM = 64 * TW;
+  us2 m2 = {0, 0};
+#pragma unroll
+  for (int i = 0; i < CH; ++i) m2 = chunk_amax(h[i], m2);
+  uint32_t m = m2.x > m2.y ? m2.x : m2.y;
+  m = wave_max_u32(m);
+  if (TW > 1) {
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = red[0];
+#pragma unroll
+    for (int w = 1; w < TW; ++w) m = m > red[w] ? m : red[w];
+  }
+  if (!row_ok) return;
+  float s, r, p;
+  bool tiny;
+  unit_scale(m, s, r, p, tiny);
+  if (team_lane == 0) scale[row] = s;
+  uint2* qr = q + row * nch;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int64_t c = (int64_t)i * TEAM + team_lane;
+    if (c < nch) qr[c] = tiny ? quant8<true>(h[i], s, r, p) : quant8<false>(h[i], s, r, p);
+  }
+}
+
+// One team of TW waves per row (TW = 1: four rows per 256-thread block).
+template <int CH, int TW>
+__global__ __launch_bounds__(TW >= 4 ? 64 * TW : 256) void silu_mul_quant_kernel(
+    const uint4* __restrict__ gu, int64_t rows, int64_t I, uint2* __restrict__ q,
+    float* __restrict__ scale) {
+  constexpr int TEAM = 64 * TW;
+  constexpr int RPB = TW >= 4 ? 1 : 4 / TW;
+  __shared__ uint32_t red[TW >= 4 ? TW : 4];
+  const int tid = threadIdx.x, tl = tid % TEAM;
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / TEAM;
+  const int64_t nch = I >> 3;
+  const bool row_ok = row < rows;
+  const uint4* gr = gu + (row_ok ? row : 0) * 2 * nch;
+  uint4 h[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int64_t c = (int64_t)i * TEAM + tl;
+    h[i] = (row_ok && c < nch) ? silu_mul8(ld16(gr + c), ld16(gr + nch + c))
+                               : make_uint4(0, 0, 0, 0);
+  }
+  quantize_team<CH, TW>(h, row_ok, row, nch, tl, red, q, scale);
+}
+
+template <int CH, int TW>
+__global__ __launch_bounds__(TW >= 4 ? 64 * TW : 256) void rmsnorm_quant_kernel(
+    const uint4* __restrict__ x, const uint4* __restrict__ gamma, int64_t rows,
+    int64_t H, double eps, uint2* __restrict__ q, float* __restrict__ scale) {
+  constexpr int TEAM = 64 * TW;
+  constexpr int RPB = TW >= 4 ? 1 : 4 / TW;
+  __shared__ uint32_t red[TW >= 4 ? TW : 4];
+  __shared__ double reds[TW >= 4 ? TW : 4];
+  const int tid = threadIdx.x, tl = tid % TEAM;
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / TEAM;
+  const int64_t nch = H >> 3;
+  const bool row_ok = row < rows;
+  const uint4* xr = x + (row_ok ? row : 0) * nch;
+  uint4 h[CH];
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int64_t c = (int64_t)i * TEAM + tl;
+    h[i] = (row_ok && c < nch) ? ld16(xr + c) : make_uint4(0, 0, 0, 0);
+    ss += chunk_sumsq(h[i]);
+  }
+  ss = wave_sum_f64(ss);
+  if (TW > 1) {
+    if ((tid & 63) == 0) reds[tid >> 6] = ss;
+    __syncthreads();
+    ss = reds[0];
+#pragma unroll
+    for (int w = 1; w < TW; ++w) ss += reds[w];   // fixed order
+  }
+  const double r64 = 1.0 / sqrt(ss / (double)H + eps);
+  const float r32 = (float)r64;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int64_t c = (int64_t)i * TEAM + tl;
+    if (row_ok && c < nch) {
+      const uint4 gv = ld16(gamma + c);
+      const uint32_t xw[4] = {h[i].x, h[i].y, h[i].z, h[i].w};
+      const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o[k] = rms1(bf16lo(xw[k]), bf16lo(gw[k]), r32, r64) |
+               (rms1(bf16hi(xw[k]), bf16hi(gw[k]), r32, r64) << 16);
+      h[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+  quantize_team<CH, TW>(h, row_ok, row, nch, tl, red, q, scale);
+}
+
+// ---- static calibration: exact order statistics by two radix passes -------
+// bf16 bits -> 16-bit key with the same order as the values (-0 below +0).
+__device__ __forceinline__ uint32_t okey(uint32_t b) {
+  return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+}
+__device__ __forceinline__ uint32_t okey_inv(uint32_t k) {
+  return (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+}
+
+constexpr int kHistBlocks = 1024;
+
+// Pass 1: per-block histogram of the key's high byte. Pass 2: per-block
+// histograms of the low byte of the keys whose high byte is sel[0] / sel[2].
+template <bool SECOND>
+__global__ __launch_bounds__(256) void calib_hist_kernel(const uint4* __restrict__ x,
+                                                         int64_t nch, const uint32_t* sel,
+                                                         uint32_t* __restrict__ part) {
+  __shared__ uint32_t hst[SECOND ? 512 : 256];
+  const int tid = threadIdx.x;
+  for (int b = tid; b < (SECOND ? 512 : 256); b += 256) hst[b] = 0;
+  uint32_t hb_lo = 0, hb_hi = 0;
+  if (SECOND) { hb_lo = sel[0]; hb_hi = sel[2]; }
+  __syncthreads();
+  for (int64_t c = (int64_t)blockIdx.x * 256 + tid; c < nch; c += (int64_t)gridDim.x * 256) {
+    const uint4 v = ld16(x + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t k = okey((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+      if (!SECOND) {
+        atomicAdd(&hst[k >> 8], 1u);
+      } else {
+        if ((k >> 8) == hb_lo) atomicAdd(&hst[k & 255u], 1u);
+        if ((k >> 8) == hb_hi) atomicAdd(&hst[256 + (k & 255u)], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  for (int b = tid; b < (SECOND ? 512 : 256); b += 256)
+    part[(int64_t)blockIdx.x * (SECOND ? 512 : 256) + b] = hst[b];
+}
+
+// Sum the per-block histograms (fixed order) and find, for ranks k_lo and
+// k_hi (1-based), the bucket and the rank inside it. One block of 256.
+// SECOND: the buckets are low bytes; write the scale.
+template <bool SECOND>
+__global__ __launch_bounds__(256) void calib_select_kernel(const uint32_t* __restrict__ part,
+                                                           int nblk, int64_t k_lo, int64_t k_hi,
+                                                           uint32_t* sel, float* scale_out) {
+  __shared__ int64_t cnt[2][256];
+  const int tid = threadIdx.x;
+  constexpr int W = SECOND ? 512 : 256;
+  for (int h = 0; h < (SECOND ? 2 : 1); ++h) {
+    int64_t s = 0;
+    for (int b = 0; b < nblk; ++b) s += part[(int64_t)b * W + h * 256 + tid];
+    cnt[h][tid] = s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int64_t ranks[2] = {k_lo, k_hi};
+    uint32_t out[4];
+    for (int j = 0; j < 2; ++j) {
+      const int h = SECOND ? j : 0;
+      int64_t k = SECOND ? (int64_t)sel[2 * j + 1] : ranks[j];
+      int b = 0;
+      int64_t before = 0;
+      for (; b < 256; ++b) {
+        if (before + cnt[h][b] >= k) break;
+        before += cnt[h][b];
+      }
+      if (b > 255) b = 255;   // empty input (k = 0 cannot be reached otherwise)
+      out[2 * j] = (uint32_t)b;
+      out[2 * j + 1] = (uint32_t)(k - before);
+    }
+    if (!SECOND) {
+      for (int j = 0; j < 4; ++j) sel[j] = out[j];
+    } else {
+      const uint32_t key_lo = (sel[0] << 8) | out[0];
+      const uint32_t key_hi = (sel[2] << 8) | out[2];
+      const float vlo = fabsf(__uint_as_float(okey_inv(key_lo) << 16));
+      const float vhi = fabsf(__uint_as_float(okey_inv(key_hi) << 16));
+      const float amax = (k_hi > 0) ? fmaxf(vlo, vhi) : 0.0f;
+      scale_out[0] = amax / kE4M3Max;            // correctly rounded: RN(amax/448)
+    }
+  }
+}
+
+// Static quantization with one fp32 scale for the whole tensor: codes of
+// x / s, saturating at +-448 (clamped before the hardware conversion, whose
+// own saturation does not reach beyond 464).
+template <bool PRE>
+__device__ __forceinline__ uint2 quant8_sat(uint4 raw, float s, float r, float p) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float x[8], y[8], yc[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    y[i] = (PRE ? x[i] * p : x[i]) * r;
+    yc[i] = __builtin_fminf(__builtin_fmaxf(y[i], -460.0f), 460.0f);
+  }
+  uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(yc[0], yc[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(yc[2], yc[3], lo, true);
+  uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(yc[4], yc[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(yc[6], yc[7], hi, true);
+  const float sp = PRE ? s * p : s;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (needs_fixup(y[i])) {
+      uint32_t& word = (i < 4) ? lo : hi;
+      const int sh = 8 * (i & 3);
+      const float ax = __builtin_fabsf(PRE ? x[i] * p : x[i]);
+      const uint32_t mag = exact_mag(ax, sp, __builtin_fabsf(y[i]));
+      const uint32_t code = mag | ((__float_as_uint(x[i]) >> 24) & 0x80u);
+      word = (word & ~(0xFFu << sh)) | (code << sh);
+    }
+  }
+  return make_uint2(lo, hi);
+}
+
+__global__ __launch_bounds__(256) void quant_static_kernel(const uint4* __restrict__ x,
+                                                           int64_t nch, const float* sptr,
+                                                           uint2* __restrict__ q) {
+  const float s = *sptr;
+  const bool tiny = s < kTinyScale && s > 0.0f;
+  const float p = tiny ? kPreScale : 1.0f;
+  const float r = s > 0.0f ? 1.0f / (s * p) : 0.0f;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nch;
+       c += (int64_t)gridDim.x * 256)
+    q[c] = tiny ? quant8_sat<true>(ld16(x + c), s, r, p) : quant8_sat<false>(ld16(x + c), s, r, p);
+}
+
+// ---- FP8 KV cache: per-token quantization, rows scattered by slot ---------
+template <int CH, int TW>
+__global__ __launch_bounds__(TW >= 4 ? 64 * TW : 256) void kv_quant_kernel(
+    const uint4* __restrict__ x, int64_t T, int64_t width, const int64_t* __restrict__ slots,
+    int64_t n_slots, uint2* __restrict__ cache, float* __restrict__ cscale) {
+  constexpr int TEAM = 64 * TW;
+  constexpr int RPB = TW >= 4 ? 1 : 4 / TW;
+  __shared__ uint32_t red[TW >= 4 ? TW : 4];
+  const int tid = threadIdx.x, tl = tid % TEAM;
+  const int64_t t = (int64_t)blockIdx.x * RPB + tid / TEAM;
+  const int64_t nch = width >> 3;
+  const int64_t slot = t < T ? slots[t] : -1;
+  const bool row_ok = slot >= 0 && slot < n_slots;   // out-of-range slots are skipped
+  const uint4* xr = x + (t < T ? t : 0) * nch;
+  uint4 h[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int64_t c = (int64_t)i * TEAM + tl;
+    h[i] = (row_ok && c < nch) ? ld16(xr + c) : make_uint4(0, 0, 0, 0);
+  }
+  quantize_team<CH, TW>(h, row_ok, row_ok ? slot : 0, nch, tl, red, cache, cscale);
+}
+
+// Row-team launch ladder shared by the row kernels: TW = 1 for rows of up to
+// 512 chunks (4096 values), else 4 waves, then 16; CH chunks per lane.
+template <template <int, int> class Launch, typename... A>
+int launch_ladder(int64_t nch, A... a) {
+  if (nch <= 64) { Launch<1, 1>::go(a...); return 0; }
+  if (nch <= 128) { Launch<2, 1>::go(a...); return 0; }
+  if (nch <= 256) { Launch<4, 1>::go(a...); return 0; }
+  if (nch <= 512) { Launch<8, 1>::go(a...); return 0; }
+  if (nch <= 1024) { Launch<4, 4>::go(a...); return 0; }
+  if (nch <= 2048) { Launch<8, 4>::go(a...); return 0; }
+  if (nch <= 4096) { Launch<4, 16>::go(a...); return 0; }
+  if (nch <= 8192) { Launch<8, 16>::go(a...); return 0; }
+  return -1;
+}
+
+template <int CH, int TW>
+struct RowsGrid {
+  static dim3 blocks(int64_t rows) {
+    constexpr int RPB = TW >= 4 ? 1 : 4 / TW;
+    return dim3((unsigned)((rows + RPB - 1) / RPB));
+  }
+  static dim3 threads() { return dim3(TW >= 4 ? 64 * TW : 256); }
+};
+
+template <int CH, int TW>
+struct SiluLaunch {
+  static void go(const void* gu, int64_t rows, int64_t I, uint8_t* q, float* s, hipStream_t st) {
+    hipLaunchKernelGGL((silu_mul_quant_kernel<CH, TW>), (RowsGrid<CH, TW>::blocks(rows)),
+                       (RowsGrid<CH, TW>::threads()), 0, st, (const uint4*)gu, rows, I,
+                       (uint2*)q, s);
+  }
+};
+template <int CH, int TW>
+struct RmsLaunch {
+  static void go(const void* x, const void* g, int64_t rows, int64_t H, double eps,
+                 uint8_t* q, float* s, hipStream_t st) {
+    hipLaunchKernelGGL((rmsnorm_quant_kernel<CH, TW>), (RowsGrid<CH, TW>::blocks(rows)),
+                       (RowsGrid<CH, TW>::threads()), 0, st, (const uint4*)x,
+                       (const uint4*)g, rows, H, eps, (uint2*)q, s);
+  }
+};
+template <int CH, int TW>
+struct KvLaunch {
+  static void go(const void* x, int64_t T, int64_t width, const int64_t* slots,
+                 int64_t n_slots, uint8_t* cache, float* cs, hipStream_t st) {
+    hipLaunchKernelGGL((kv_quant_kernel<CH, TW>), (RowsGrid<CH, TW>::blocks(T)),
+                       (RowsGrid<CH, TW>::threads()), 0, st, (const uint4*)x, T, width,
+                       slots, n_slots, (uint2*)cache, cs);
+  }
+};
+
+}  // namespace
+
+int launch_silu_mul_quant(const void* gu, int64_t rows, int64_t I, uint8_t* q,
+                          float* scale, hipStream_t st) {
+  return launch_ladder<SiluLaunch>(I / 8, gu, rows, I, q, scale, st);
+}
+
+int launch_rmsnorm_quant(const void* x, const void* gamma, int64_t rows, int64_t H,
+                         double eps, uint8_t* q, float* scale, hipStream_t st) {
+  return launch_ladder<RmsLaunch>(H / 8, x, gamma, rows, H, eps, q, scale, st);
+}
+
+int launch_kv_quant(const void* x, int64_t T, int64_t width, const int64_t* slots,
+                    int64_t n_slots, uint8_t* cache, float* cscale, hipStream_t st) {
+  return launch_ladder<KvLaunch>(width / 8, x, T, width, slots, n_slots, cache, cscale, st);
+}
+
+size_t calib_workspace_bytes() {
+  return (size_t)kHistBlocks * (256 + 512) * 4 + 256;
+}
+
+void launch_calib_scale(const void* x, int64_t n, int64_t k_lo, int64_t k_hi,
+                        float* scale_out, void* ws, hipStream_t st) {
+  const int64_t nch = n / 8;
+  int nblk = (int)((nch + 255) / 256);
+  if (nblk > kHistBlocks) nblk = kHistBlocks;
+  if (nblk < 1) nblk = 1;
+  uint32_t* part1 = static_cast<uint32_t*>(ws);
+  uint32_t* part2 = part1 + (size_t)kHistBlocks * 256;
+  uint32_t* sel = part2 + (size_t)kHistBlocks * 512;
+  hipLaunchKernelGGL((calib_hist_kernel<false>), dim3(nblk), dim3(256), 0, st,
+                     (const uint4*)x, nch, (const uint32_t*)sel, part1);
+  hipLaunchKernelGGL((calib_select_kernel<false>), dim3(1), dim3(256), 0, st,
+                     (const uint32_t*)part1, nblk, k_lo, k_hi, sel, scale_out);
+  hipLaunchKernelGGL((calib_hist_kernel<true>), dim3(nblk), dim3(256), 0, st,
+                     (const uint4*)x, nch, (const uint32_t*)sel, part2);
+  hipLaunchKernelGGL((calib_select_kernel<true>), dim3(1), dim3(256), 0, st,
+                     (const uint32_t*)part2, nblk, k_lo, k_hi, sel, scale_out);
+}
+
+void launch_quant_static(const void* x, int64_t n, const float* scale, uint8_t* q,
+                         hipStream_t st) {
+  const int64_t nch = n / 8;
+  int64_t blocks = (nch + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(quant_static_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                     (const uint4*)x, nch, scale, (uint2*)q);
+}
+
+}  // namespace fp8dq

@@ -37,4 +37,18 @@ void launch_gemm_decode(const uint8_t* qx, const float* sx, const uint8_t* qw,
                         int64_t N, int64_t K, bool block, const DecodePlan& p,
                         hipStream_t st);
 
+// Fused producers, static calibration, KV cache (fused_quant.hip). The row
+// launchers return -1 when a row is longer than 65536 values.
+int launch_silu_mul_quant(const void* gu, int64_t rows, int64_t I, uint8_t* q,
+                          float* scale, hipStream_t st);
+int launch_rmsnorm_quant(const void* x, const void* gamma, int64_t rows, int64_t H,
+                         double eps, uint8_t* q, float* scale, hipStream_t st);
+int launch_kv_quant(const void* x, int64_t T, int64_t width, const int64_t* slots,
+                    int64_t n_slots, uint8_t* cache, float* cscale, hipStream_t st);
+size_t calib_workspace_bytes();
+void launch_calib_scale(const void* x, int64_t n, int64_t k_lo, int64_t k_hi,
+                        float* scale_out, void* ws, hipStream_t st);
+void launch_quant_static(const void* x, int64_t n, const float* scale, uint8_t* q,
+                         hipStream_t st);
+
 }  // namespace fp8dq

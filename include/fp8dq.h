@@ -162,6 +162,76 @@ int fp8_linear_block(const void* x_bf16, const uint8_t* qw, const float* sw,
 size_t fp8_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t block,
                            uint32_t flags);
 
+/* ------------------------------------------------------------------------
+ * Producers fused with the per-token quantizer, static calibration and the
+ * FP8 KV cache ("Llama 3 精读实录" page). In the fused producers the bf16
+ * value h that gets quantized is the correctly rounded bf16 of the exact
+ * real formula (ties to even); its FP8 codes and scales then follow the
+ * per-token rules of fp8_quant_act. Row kernels take rows of at most 65536
+ * values (FP8DQ_ERR_SHAPE beyond). Same conventions as above otherwise.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * fp8_silu_mul_quant -- SwiGLU's gated product, quantized per token:
+ *   h[r,i] = bf16( silu(g[r,i]) * u[r,i] ),  silu(g) = g / (1 + e^-g),
+ *   g = gu[r, 0:I], u = gu[r, I:2I] (gate | up, as one fused gate_up GEMM
+ *   writes them); q [rows, I] and scale [rows] as fp8_quant_act(h, group 0).
+ * Source: §1.3 of the page (gate and up branches computed separately, then
+ * multiplied elementwise). h is not written out.
+ * Size rules: rows >= 0; I > 0, I % 8 == 0, I <= 65536.
+ */
+int fp8_silu_mul_quant(const void* gu_bf16, int64_t rows, int64_t I, uint8_t* q,
+                       float* scale, void* stream);
+
+/*
+ * fp8_rmsnorm_quant -- RMSNorm, quantized per token:
+ *   h[r,i] = bf16( gamma[i] * x[r,i] / sqrt(mean_i(x[r,i]^2) + eps) ),
+ *   x bf16 [rows, H], gamma bf16 [H]; q [rows, H], scale [rows].
+ * Source: §1.3 of the page (eps = 1e-5, norm before attention and the MLP;
+ * §5.3 keeps the norm itself in bf16). eps >= 0 (FP8DQ_ERR_SHAPE otherwise).
+ * Size rules: rows >= 0; H > 0, H % 8 == 0, H <= 65536.
+ */
+int fp8_rmsnorm_quant(const void* x_bf16, const void* gamma_bf16, int64_t rows, int64_t H,
+                      double eps, uint8_t* q, float* scale, void* stream);
+
+/*
+ * fp8_calib_scale -- static per-tensor scale from percentile calibration:
+ *   amax = max(|x_(k_lo)|, |x_(k_hi)|), k = ceil(p * n) clamped to [1, n]
+ *   (nearest-rank order statistics of the n values, p = permille / 1000),
+ *   *scale_out = RN_fp32(amax / 448)   (0 when n == 0).
+ * Source: §2.2 of the page (P99.9 / P0.1 percentiles of a calibration set
+ * as the dynamic range instead of the maximum): lo 1, hi 999 by default.
+ *   x: bf16 [n]; scale_out: device fp32 [1]; ws: fp8_calib_workspace_bytes
+ *   bytes (contents need no initialisation).
+ * Size rules: 0 <= n < 2^32, n % 8 == 0; 0 <= lo <= hi <= 1000.
+ */
+size_t fp8_calib_workspace_bytes(int64_t n);
+int fp8_calib_scale(const void* x_bf16, int64_t n, int32_t lo_permille, int32_t hi_permille,
+                    float* scale_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * fp8_quant_static -- E4M3 codes of x / s with one static scale s (device
+ * fp32 [1], e.g. from fp8_calib_scale): nearest with ties to the even code,
+ * saturating at +-448 (0x7E / 0xFE), sign of zero kept; s == 0 gives +-0.
+ *   x: bf16 [n] -> q: uint8 [n].  Size rules: n >= 0, n % 8 == 0.
+ */
+int fp8_quant_static(const void* x_bf16, int64_t n, const float* scale, uint8_t* q,
+                     void* stream);
+
+/*
+ * fp8_kv_cache_quant -- FP8 KV cache write: each token row of K and V
+ * (bf16 [T, width], width = KV heads * head dim) is quantized per token as
+ * in fp8_quant_act and stored in cache row slots[t] of k_cache / v_cache
+ * (uint8 [n_slots, width]) with its scale in k_scale / v_scale (fp32
+ * [n_slots]); tokens whose slot is negative or >= n_slots are not written.
+ * slots: device int64 [T]. Source: §4.1 of the page (FP8 also compresses
+ * the KV cache). Size rules: T >= 0; width > 0, width % 8 == 0,
+ * width <= 65536; n_slots >= 0.
+ */
+int fp8_kv_cache_quant(const void* k_bf16, const void* v_bf16, int64_t T, int64_t width,
+                       const int64_t* slots, int64_t n_slots, uint8_t* k_cache,
+                       uint8_t* v_cache, float* k_scale, float* v_scale, void* stream);
+
 /* fp8_status_string -- static text for a status code (never NULL). */
 const char* fp8_status_string(int status);
 

@@ -107,6 +107,49 @@ def test_linear_errors(L, fn):
     assert f(None, None, None, None, 0, 128, 128, None, None, 0, None, 0, None) == 0
 
 
+def test_fused_producer_errors(L):
+    f = L.fp8_silu_mul_quant
+    assert f(None, 4, 256, A, A, None) == -1
+    assert f(A, 4, 100, A, A, None) == -2          # I % 8
+    assert f(A, 4, 65536 + 8, A, A, None) == -2    # row too long
+    assert f(A, -1, 256, A, A, None) == -2
+    assert f(MIS, 4, 256, A, A, None) == -3
+    assert f(None, 0, 256, None, None, None) == 0   # empty
+    g = L.fp8_rmsnorm_quant
+    assert g(A, None, 4, 256, 1e-5, A, A, None) == -1
+    assert g(A, A, 4, 12, 1e-5, A, A, None) == -2
+    assert g(A, A, 4, 256, -1.0, A, A, None) == -2    # negative eps
+    assert g(A, A, 4, 256, float("nan"), A, A, None) == -2
+    assert g(A, MIS, 4, 256, 1e-5, A, A, None) == -3
+    assert g(None, None, 0, 256, 1e-5, None, None, None) == 0
+
+
+def test_calibration_and_static_errors(L):
+    need = F.fp8_calib_workspace_bytes(4096)
+    assert need > 0
+    c = L.fp8_calib_scale
+    assert c(A, 4096, 1, 999, A, None, need, None) == -1
+    assert c(A, 4096, 1, 999, A, A, need - 4, None) == -4
+    assert c(A, 4095, 1, 999, A, A, need, None) == -2      # n % 8
+    assert c(A, 4096, 999, 1, A, A, need, None) == -2      # lo > hi
+    assert c(A, 4096, 1, 1001, A, A, need, None) == -2
+    assert c(A, 1 << 32, 1, 999, A, A, need, None) == -2
+    assert c(MIS, 4096, 1, 999, A, A, need, None) == -3
+    s = L.fp8_quant_static
+    assert s(A, 100, A, A, None) == -2
+    assert s(None, 64, A, A, None) == -1
+    assert s(A, 0, None, None, None) == 0
+
+
+def test_kv_cache_errors(L):
+    k = L.fp8_kv_cache_quant
+    assert k(A, A, 8, 1024, None, 16, A, A, A, A, None) == -1
+    assert k(A, A, 8, 1000 + 4, A, 16, A, A, A, A, None) == -2
+    assert k(A, A, 8, 1024, A, -1, A, A, A, A, None) == -2
+    assert k(A, MIS, 8, 1024, A, 16, A, A, A, A, None) == -3
+    assert k(None, None, 0, 1024, None, 16, None, None, None, None, None) == 0
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     from fp8_dynamic_quantized_amd import _binding
     monkeypatch.setattr(_binding, "_lib", None)
