@@ -18,6 +18,9 @@ Also reported:
   decode        the Llama-3.1-70B decode linears at M in {1, 8, 32, 64}:
                 end-to-end fp8_linear weight GB/s with cold weights
                 (rotated copies well beyond the 256 MB last-level cache);
+  next_rows     SwiGLU->FP8 and RMSNorm->FP8 fused quantizers, percentile
+                calibration over a 512 x 2048-token set, static quantization
+                and the FP8 KV-cache write, in GB/s of algorithmic bytes;
   cpu_baseline  the CPU oracle timed on a bounded sample of the workload.
 
 Other modes (profiling helpers, no JSON line):
@@ -255,6 +258,86 @@ def bench_decode(F, torch, batches=7, per_batch=20, warm=5):
     return out
 
 
+def _time_us(torch, fn, reps=20, warm=3, batches=5):
+    """Median over batches of the average duration of `reps` back-to-back
+    launches (HIP events on the current stream)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warm):
+        fn()
+    times = []
+    for _ in range(batches):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / reps)
+    return statistics.median(times)
+
+
+def bench_next_rows(F, torch):
+    """The producers fused with the quantizer, static calibration and the
+    FP8 KV-cache write, at Llama-3.1-8B sizes (HBM-bound: algorithmic bytes
+    moved per launch / time)."""
+    import synth
+    out = {}
+
+    def rec(name, us, nbytes, shape):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"us": round(us, 2), "gbs": round(gbs, 1),
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": int(nbytes), "shape": shape}
+        log(f"  {name}: {us:.1f} us, {gbs:.0f} GB/s")
+
+    M, inner, hidden = 4096, 14336, 4096
+    gu = to_dev(synth.activations(M, 2 * inner, 61, 62), torch)
+    q = torch.empty((M, inner), dtype=torch.uint8, device="cuda")
+    s = torch.empty((M,), dtype=torch.float32, device="cuda")
+    us = _time_us(torch, lambda: F.fp8_silu_mul_quant(gu, q=q, scale=s))
+    rec("silu_mul_quant", us, M * 2 * inner * 2 + M * inner + 4 * M,
+        f"gate_up out [{M},{2 * inner}] -> codes [{M},{inner}]")
+    del gu, q
+
+    x = to_dev(synth.activations(M, hidden, 63, 64), torch)
+    gamma = torch.ones(hidden, dtype=torch.bfloat16, device="cuda")
+    q = torch.empty((M, hidden), dtype=torch.uint8, device="cuda")
+    us = _time_us(torch, lambda: F.fp8_rmsnorm_quant(x, gamma, q=q, scale=s))
+    rec("rmsnorm_quant", us, M * hidden * 3 + hidden * 2 + 4 * M,
+        f"[{M},{hidden}] -> codes")
+
+    # calibration set: 512 samples x 2048 tokens of one layer's input (4096 wide)
+    ncal = 512 * 2048 * hidden
+    g = torch.Generator(device="cuda")
+    g.manual_seed(synth.seed_of(6, 0, 0, 0))
+    cal = (torch.randn((512 * 2048, hidden), generator=g, device="cuda")).to(torch.bfloat16)
+    scale = torch.empty((1,), dtype=torch.float32, device="cuda")
+    ws = torch.empty(F.fp8_calib_workspace_bytes(ncal), dtype=torch.uint8, device="cuda")
+    us = _time_us(torch, lambda: F.fp8_calib_scale(cal, 1, 999, scale=scale, ws=ws), reps=3,
+                  warm=1, batches=3)
+    rec("calib_scale", us, 2 * ncal * 2, f"{ncal} values (512 x 2048 tokens x {hidden}), 2 passes")
+    del cal, ws
+    torch.cuda.empty_cache()
+    us = _time_us(torch, lambda: F.fp8_quant_static(x, scale, q=q))
+    rec("quant_static", us, M * hidden * 3, f"[{M},{hidden}] -> codes")
+    del x, q
+
+    T, width, n_slots = 4096, 8 * 128, 8192
+    k = to_dev(synth.activations(T, width, 65, 66), torch)
+    v = to_dev(synth.activations(T, width, 67, 68), torch)
+    slots = torch.randperm(n_slots, generator=torch.Generator().manual_seed(69))[:T].cuda()
+    kc = torch.empty((n_slots, width), dtype=torch.uint8, device="cuda")
+    vc = torch.empty_like(kc)
+    ks = torch.empty((n_slots,), dtype=torch.float32, device="cuda")
+    vs = torch.empty_like(ks)
+    us = _time_us(torch, lambda: F.fp8_kv_cache_quant(k, v, slots, kc, vc, ks, vs))
+    rec("kv_cache_quant", us, 2 * (T * width * 3 + 4 * T) + 8 * T,
+        f"K,V [{T},{width}] -> cache rows")
+    del k, v, kc, vc
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration(torch):
     src = torch.randint(0, 255, (COPY_BYTES,), dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -307,6 +390,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-regime section")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the fused-producer / calibration / KV-cache section")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-profile", metavar="DIR")
     args = ap.parse_args()
@@ -373,6 +458,9 @@ def main():
     }
     if not args.no_decode:
         out["decode"] = bench_decode(F, torch)
+    if not args.no_next:
+        log("fused producers, calibration, KV cache ...")
+        out["next_rows"] = bench_next_rows(F, torch)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(synth.SHAPES["c2"], args.cpu_rows,

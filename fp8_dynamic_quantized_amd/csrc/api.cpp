@@ -201,7 +201,7 @@ size_t fp8_calib_workspace_bytes(int64_t n) {
 
 int fp8_calib_scale(const void* x_bf16, int64_t n, int32_t lo_permille, int32_t hi_permille,
                     float* scale_out, void* ws, size_t ws_bytes, void* stream) {
-  if (n < 0 || (n % 8) != 0 || n >= (int64_t(1) << 32)) return FP8DQ_ERR_SHAPE;
+  if (n < 0 || (n % 8) != 0 || n >= (int64_t(1) << 40)) return FP8DQ_ERR_SHAPE;
   if (lo_permille < 0 || hi_permille > 1000 || lo_permille > hi_permille)
     return FP8DQ_ERR_SHAPE;
   if ((n > 0 && !x_bf16) || !scale_out || !ws) return FP8DQ_ERR_NULL;

@@ -262,13 +262,13 @@ constexpr int kHistBlocks = 1024;
 // histograms of the low byte of the keys whose high byte is sel[0] / sel[2].
 template <bool SECOND>
 __global__ __launch_bounds__(256) void calib_hist_kernel(const uint4* __restrict__ x,
-                                                         int64_t nch, const uint32_t* sel,
+                                                         int64_t nch, const int64_t* sel,
                                                          uint32_t* __restrict__ part) {
   __shared__ uint32_t hst[SECOND ? 512 : 256];
   const int tid = threadIdx.x;
   for (int b = tid; b < (SECOND ? 512 : 256); b += 256) hst[b] = 0;
   uint32_t hb_lo = 0, hb_hi = 0;
-  if (SECOND) { hb_lo = sel[0]; hb_hi = sel[2]; }
+  if (SECOND) { hb_lo = (uint32_t)sel[0]; hb_hi = (uint32_t)sel[2]; }
   __syncthreads();
   for (int64_t c = (int64_t)blockIdx.x * 256 + tid; c < nch; c += (int64_t)gridDim.x * 256) {
     const uint4 v = ld16(x + c);
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(256) void calib_hist_kernel(const uint4* __restrict
 template <bool SECOND>
 __global__ __launch_bounds__(256) void calib_select_kernel(const uint32_t* __restrict__ part,
                                                            int nblk, int64_t k_lo, int64_t k_hi,
-                                                           uint32_t* sel, float* scale_out) {
+                                                           int64_t* sel, float* scale_out) {
   __shared__ int64_t cnt[2][256];
   const int tid = threadIdx.x;
   constexpr int W = SECOND ? 512 : 256;
@@ -307,10 +307,10 @@ __global__ __launch_bounds__(256) void calib_select_kernel(const uint32_t* __res
   __syncthreads();
   if (tid == 0) {
     int64_t ranks[2] = {k_lo, k_hi};
-    uint32_t out[4];
+    int64_t out[4];
     for (int j = 0; j < 2; ++j) {
       const int h = SECOND ? j : 0;
-      int64_t k = SECOND ? (int64_t)sel[2 * j + 1] : ranks[j];
+      int64_t k = SECOND ? sel[2 * j + 1] : ranks[j];
       int b = 0;
       int64_t before = 0;
       for (; b < 256; ++b) {
@@ -318,14 +318,14 @@ __global__ __launch_bounds__(256) void calib_select_kernel(const uint32_t* __res
         before += cnt[h][b];
       }
       if (b > 255) b = 255;   // empty input (k = 0 cannot be reached otherwise)
-      out[2 * j] = (uint32_t)b;
-      out[2 * j + 1] = (uint32_t)(k - before);
+      out[2 * j] = b;
+      out[2 * j + 1] = k - before;
     }
     if (!SECOND) {
       for (int j = 0; j < 4; ++j) sel[j] = out[j];
     } else {
-      const uint32_t key_lo = (sel[0] << 8) | out[0];
-      const uint32_t key_hi = (sel[2] << 8) | out[2];
+      const uint32_t key_lo = ((uint32_t)sel[0] << 8) | (uint32_t)out[0];
+      const uint32_t key_hi = ((uint32_t)sel[2] << 8) | (uint32_t)out[2];
       const float vlo = fabsf(__uint_as_float(okey_inv(key_lo) << 16));
       const float vhi = fabsf(__uint_as_float(okey_inv(key_hi) << 16));
       const float amax = (k_hi > 0) ? fmaxf(vlo, vhi) : 0.0f;
@@ -474,7 +474,7 @@ int launch_kv_quant(const void* x, int64_t T, int64_t width, const int64_t* slot
 }
 
 size_t calib_workspace_bytes() {
-  return (size_t)kHistBlocks * (256 + 512) * 4 + 256;
+  return (size_t)kHistBlocks * (256 + 512) * 4 + 4 * sizeof(int64_t);
 }
 
 void launch_calib_scale(const void* x, int64_t n, int64_t k_lo, int64_t k_hi,
@@ -485,13 +485,13 @@ void launch_calib_scale(const void* x, int64_t n, int64_t k_lo, int64_t k_hi,
   if (nblk < 1) nblk = 1;
   uint32_t* part1 = static_cast<uint32_t*>(ws);
   uint32_t* part2 = part1 + (size_t)kHistBlocks * 256;
-  uint32_t* sel = part2 + (size_t)kHistBlocks * 512;
+  int64_t* sel = reinterpret_cast<int64_t*>(part2 + (size_t)kHistBlocks * 512);
   hipLaunchKernelGGL((calib_hist_kernel<false>), dim3(nblk), dim3(256), 0, st,
-                     (const uint4*)x, nch, (const uint32_t*)sel, part1);
+                     (const uint4*)x, nch, (const int64_t*)sel, part1);
   hipLaunchKernelGGL((calib_select_kernel<false>), dim3(1), dim3(256), 0, st,
                      (const uint32_t*)part1, nblk, k_lo, k_hi, sel, scale_out);
   hipLaunchKernelGGL((calib_hist_kernel<true>), dim3(nblk), dim3(256), 0, st,
-                     (const uint4*)x, nch, (const uint32_t*)sel, part2);
+                     (const uint4*)x, nch, (const int64_t*)sel, part2);
   hipLaunchKernelGGL((calib_select_kernel<true>), dim3(1), dim3(256), 0, st,
                      (const uint32_t*)part2, nblk, k_lo, k_hi, sel, scale_out);
 }

@@ -203,7 +203,7 @@ int fp8_rmsnorm_quant(const void* x_bf16, const void* gamma_bf16, int64_t rows, 
  * as the dynamic range instead of the maximum): lo 1, hi 999 by default.
  *   x: bf16 [n]; scale_out: device fp32 [1]; ws: fp8_calib_workspace_bytes
  *   bytes (contents need no initialisation).
- * Size rules: 0 <= n < 2^32, n % 8 == 0; 0 <= lo <= hi <= 1000.
+ * Size rules: 0 <= n < 2^40, n % 8 == 0; 0 <= lo <= hi <= 1000.
  */
 size_t fp8_calib_workspace_bytes(int64_t n);
 int fp8_calib_scale(const void* x_bf16, int64_t n, int32_t lo_permille, int32_t hi_permille,

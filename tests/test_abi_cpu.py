@@ -133,7 +133,7 @@ def test_calibration_and_static_errors(L):
     assert c(A, 4095, 1, 999, A, A, need, None) == -2      # n % 8
     assert c(A, 4096, 999, 1, A, A, need, None) == -2      # lo > hi
     assert c(A, 4096, 1, 1001, A, A, need, None) == -2
-    assert c(A, 1 << 32, 1, 999, A, A, need, None) == -2
+    assert c(A, 1 << 40, 1, 999, A, A, need, None) == -2
     assert c(MIS, 4096, 1, 999, A, A, need, None) == -3
     s = L.fp8_quant_static
     assert s(A, 100, A, A, None) == -2

@@ -116,10 +116,11 @@ def test_calib_scale(F, n, lo, hi):
     assert_scales_equal(s.cpu().numpy(), np.array([want], np.float32), "calib scale")
 
 
-def test_calib_scale_closed_form_large(F):
-    """2^28 values cycling through 1000 distinct bf16 values: the nearest-rank
-    order statistics follow from the counts, without sorting."""
-    n = 1 << 28
+@pytest.mark.parametrize("n", [1 << 28, (1 << 32) + 8000])
+def test_calib_scale_closed_form_large(F, n):
+    """n values cycling through 1000 distinct bf16 values: the nearest-rank
+    order statistics follow from the counts, without sorting. The second size
+    takes the ranks beyond 32 bits."""
     distinct = np.unique(synth.bf16_bits_to_f32(bits_of(
         np.random.default_rng(11).standard_normal(4000) * 4)))[:1000]
     assert distinct.size == 1000
