@@ -37,6 +37,8 @@ _SIGS = {
     "fp8_silu_mul_quant": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p]),
     "fp8_rmsnorm_quant": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, ctypes.c_double, _c_p,
                                          _c_p, _c_p]),
+    "fp8_silu_mul": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p]),
+    "fp8_rmsnorm": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, ctypes.c_double, _c_p, _c_p]),
     "fp8_calib_workspace_bytes": (ctypes.c_size_t, [_i64]),
     "fp8_calib_scale": (ctypes.c_int, [_c_p, _i64, ctypes.c_int32, ctypes.c_int32, _c_p,
                                        _c_p, ctypes.c_size_t, _c_p]),
@@ -260,6 +262,34 @@ def fp8_rmsnorm_quant(x, gamma, eps: float = RMS_EPS, q=None, scale=None, stream
         _ptr(x), _ptr(gamma), rows, hidden, float(eps), _ptr(q), _ptr(scale),
         _stream(x, stream)))
     return q, scale
+
+
+def fp8_silu_mul(gu, out=None, stream=None):
+    """gu bf16 [rows, 2I] = (gate | up) -> bf16(silu(gate) * up) [rows, I]."""
+    import torch
+    rows, two_i = gu.shape
+    _need(gu, torch.bfloat16, (rows, two_i), "gu")
+    if two_i % 2:
+        raise ValueError("gu: the column count must be even (gate | up)")
+    inner = two_i // 2
+    out = torch.empty((rows, inner), dtype=torch.bfloat16, device=gu.device) if out is None else out
+    _need(out, torch.bfloat16, (rows, inner), "out")
+    _check("fp8_silu_mul", lib().fp8_silu_mul(_ptr(gu), rows, inner, _ptr(out),
+                                              _stream(gu, stream)))
+    return out
+
+
+def fp8_rmsnorm(x, gamma, eps: float = RMS_EPS, out=None, stream=None):
+    """x bf16 [rows, H], gamma bf16 [H] -> bf16(gamma * x / sqrt(mean(x^2) + eps))."""
+    import torch
+    rows, hidden = x.shape
+    _need(x, torch.bfloat16, (rows, hidden), "x")
+    _need(gamma, torch.bfloat16, (hidden,), "gamma")
+    out = torch.empty((rows, hidden), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _need(out, torch.bfloat16, (rows, hidden), "out")
+    _check("fp8_rmsnorm", lib().fp8_rmsnorm(_ptr(x), _ptr(gamma), rows, hidden, float(eps),
+                                            _ptr(out), _stream(x, stream)))
+    return out
 
 
 def fp8_calib_workspace_bytes(n: int) -> int:

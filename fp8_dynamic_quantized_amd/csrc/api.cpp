@@ -195,6 +195,30 @@ int fp8_rmsnorm_quant(const void* x_bf16, const void* gamma_bf16, int64_t rows, 
   return launch_status();
 }
 
+int fp8_silu_mul(const void* gu_bf16, int64_t rows, int64_t I, void* h_bf16, void* stream) {
+  if (rows < 0 || I <= 0 || (I % 8) != 0 || I > kMaxFusedRow) return FP8DQ_ERR_SHAPE;
+  if (rows > INT32_MAX) return FP8DQ_ERR_SHAPE;
+  if (rows == 0) return FP8DQ_OK;
+  if (!gu_bf16 || !h_bf16) return FP8DQ_ERR_NULL;
+  if (!aligned16(gu_bf16) || !aligned16(h_bf16)) return FP8DQ_ERR_ALIGN;
+  if (fp8dq::launch_silu_mul(gu_bf16, rows, I, h_bf16, as_stream(stream)) != 0)
+    return FP8DQ_ERR_SHAPE;
+  return launch_status();
+}
+
+int fp8_rmsnorm(const void* x_bf16, const void* gamma_bf16, int64_t rows, int64_t H, double eps,
+                void* h_bf16, void* stream) {
+  if (rows < 0 || H <= 0 || (H % 8) != 0 || H > kMaxFusedRow) return FP8DQ_ERR_SHAPE;
+  if (rows > INT32_MAX) return FP8DQ_ERR_SHAPE;
+  if (!(eps >= 0.0) || eps > 1.0e30) return FP8DQ_ERR_SHAPE;
+  if (rows == 0) return FP8DQ_OK;
+  if (!x_bf16 || !gamma_bf16 || !h_bf16) return FP8DQ_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(gamma_bf16) || !aligned16(h_bf16)) return FP8DQ_ERR_ALIGN;
+  if (fp8dq::launch_rmsnorm(x_bf16, gamma_bf16, rows, H, eps, h_bf16, as_stream(stream)) != 0)
+    return FP8DQ_ERR_SHAPE;
+  return launch_status();
+}
+
 size_t fp8_calib_workspace_bytes(int64_t n) {
   return n < 0 ? 0 : fp8dq::calib_workspace_bytes();
 }

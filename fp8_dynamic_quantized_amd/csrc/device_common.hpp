@@ -21,6 +21,17 @@ __device__ __forceinline__ uint4 ld16_nt(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Chunk c of p when ok, else zeros. The load is issued in every lane (from
+// chunk 0 when !ok, so p[0] must be readable), with no branch around it:
+// a lane's loads then all go out before the first of them is waited for,
+// where a branch per load makes the compiler wait for each before the next.
+template <bool NT = false>
+__device__ __forceinline__ uint4 ld16_if(const uint4* p, int64_t c, bool ok) {
+  const uint4* a = p + (ok ? c : 0);
+  const uint4 v = NT ? ld16_nt(a) : ld16(a);
+  return ok ? v : make_uint4(0, 0, 0, 0);
+}
+
 constexpr float kE4M3Max = 448.0f;  // largest finite E4M3 magnitude
 
 // 16x16 output tile, K = 128 E4M3 x E4M3 products per MFMA, fp32 accumulate.

@@ -36,13 +36,6 @@ constexpr uint32_t kMidTol = 8;  // fp32 ulps around a bf16 rounding midpoint
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16 bits when the value is safely away from a rounding midpoint
-// (the caller has checked); finite or inf.
-__device__ __forceinline__ uint32_t rne16(float h) {
-  const uint32_t b = __float_as_uint(h);
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
-
 __device__ __forceinline__ bool near_mid16(float h) {
   const uint32_t low = __float_as_uint(h) & 0xFFFFu;
   return (low - (0x8000u - kMidTol)) <= 2u * kMidTol;
@@ -83,35 +76,90 @@ __device__ __noinline__ uint32_t silu_mul_slow(float gf, float uf) {
   const double e = exp(-g);                      // inf for g < -709: h = -0 * u
   const double h = g / (1.0 + e) * u;
   return f64_to_bf16(h, [&](double m, double) {
-    // sign(|h| - |m|) = sign(h - m) * sign(m), h - m = s*((g*u - m) - m*e^-g)
-    const double a = fma(g, u, -m);              // exact: g*u has 16 bits
-    const double side = a - m * e;
-    // m * e^-g can underflow (g > 708) while g*u = m exactly: since
-    // silu(g) < g for g > 0, |h| < |g*u| = |m| then.
+    // sign(|h| - |m|) = sign(h - m) * sign(m), with
+    //   h - m = s * (g*u - m*(1 + e^-g)) = s * ((g*u - 2m) - m*expm1(-g)).
+    // g*u - 2m is exact (g*u has 16 bits and m 9, within 44 binades of each
+    // other whenever h is within 2^-36 of g*u), and expm1 keeps the small-g
+    // ties exact: there m = g*u/2 and h - m ~ m*g/2.
+    const double a = fma(g, u, -2.0 * m);
+    const double side = a - m * expm1(-g);
+    // zero when e^-g < 2^-54 (g > 37) and g*u = m: silu(g) < g for g > 0,
+    // so |h| < |m| then.
     if (side == 0.0) return g > 0.0 ? -1.0 : 0.0;
     return m > 0.0 ? side : -side;
   });
 }
 
-__device__ __forceinline__ uint32_t silu_mul1(float g, float u) {
-  if (fabsf(g) <= 64.0f) {
-    const float e = expf(-g);
-    const float h = g / (1.0f + e) * u;
-    if (!near_mid16(h) && !(tiny32(h) && g != 0.0f && u != 0.0f)) return rne16(h);
-  }
-  return silu_mul_slow(g, u);
+// e^-g for |g| <= 64 from the hardware base-2 exponential: -g * log2(e) is
+// split into p = RN(-g * L) and its remainder d (L = log2(e) as a head and a
+// tail), and 2^(p + d) is taken as 2^p * (1 + d ln 2) (|d| < 2^-17, so the
+// dropped second-order term is below 2^-35).
+__device__ __forceinline__ float exp_neg(float g) {
+  constexpr float kL = 0x1.715476p+0f;      // log2(e), head
+  constexpr float kLlo = 0x1.4ae0bep-26f;   // log2(e) - kL
+  constexpr float kLn2 = 0x1.62e430p-1f;
+  const float x = -g;
+  const float p = x * kL;
+  const float d = fmaf(x, kLlo, fmaf(x, kL, -p));
+  const float e2 = __builtin_amdgcn_exp2f(p);
+  return fmaf(e2 * kLn2, d, e2);
 }
 
-// 8 gate and 8 up values (one 16-byte chunk each) -> 8 h values (bf16).
+// 1 / (1 + e^-g), |g| <= 64, from the hardware reciprocal. Its relative error
+// over every bf16 g with |g| <= 64 stays below kSiluRecipErr (checked over
+// all of them), so h = RN(g*u * r), with g*u exact, is within
+// kSiluRecipErr + 2^-24 of the real value: under 4 fp32 ulps of h.
+__device__ __forceinline__ float silu_recip(float g) {
+  return __builtin_amdgcn_rcpf(1.0f + exp_neg(g));
+}
+
+// Elements the fast value cannot decide: |g| > 64, h near a bf16 rounding
+// midpoint, or h tiny while g*u is not zero.
+__device__ __forceinline__ bool silu_flag(float g, float gu, float h) {
+  return (__builtin_fabsf(g) > 64.0f) | near_mid16(h) | (tiny32(h) & (gu != 0.0f));
+}
+
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {   // RNE, two values
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// 8 gate and 8 up values (one 16-byte chunk each) -> 8 h values (bf16). The
+// fast value is formed for all 8 without a branch; a lane with a flagged
+// element forms those again in the exact path.
 __device__ __forceinline__ uint4 silu_mul8(uint4 gv, uint4 uv) {
-  const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
-  const uint32_t u[4] = {uv.x, uv.y, uv.z, uv.w};
-  uint32_t h[4];
+  const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+  const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
+  float g[8], u[8], h[8];
+  bool any = false;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    h[i] = silu_mul1(bf16lo(g[i]), bf16lo(u[i])) |
-           (silu_mul1(bf16hi(g[i]), bf16hi(u[i])) << 16);
-  return make_uint4(h[0], h[1], h[2], h[3]);
+  for (int i = 0; i < 4; ++i) {
+    g[2 * i] = bf16lo(gw[i]);
+    g[2 * i + 1] = bf16hi(gw[i]);
+    u[2 * i] = bf16lo(uw[i]);
+    u[2 * i + 1] = bf16hi(uw[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float gu = g[i] * u[i];
+    h[i] = gu * silu_recip(g[i]);
+    any |= silu_flag(g[i], gu, h[i]);
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pk_bf16(h[2 * i], h[2 * i + 1]);
+  if (__builtin_expect(any, 0)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (silu_flag(g[i], g[i] * u[i], h[i])) {
+        const uint32_t b = silu_mul_slow(g[i], u[i]);
+        o[i >> 1] = (i & 1) ? ((o[i >> 1] & 0xFFFFu) | (b << 16)) : ((o[i >> 1] & 0xFFFF0000u) | b);
+      }
+    }
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // ---- RMSNorm --------------------------------------------------------------
@@ -120,10 +168,44 @@ __device__ __noinline__ uint32_t rms_slow(float xf, float gf, double r) {
   return f64_to_bf16(h, [](double, double d) { return d; });  // fp64 decides
 }
 
-__device__ __forceinline__ uint32_t rms1(float x, float gm, float r32, double r64) {
-  const float h = x * r32 * gm;
-  if (!near_mid16(h) && !(tiny32(h) && x != 0.0f && gm != 0.0f)) return rne16(h);
-  return rms_slow(x, gm, r64);
+// Elements the fast value (x * r32 * gamma, within 3 fp32 ulps of the real
+// value) cannot decide: near a bf16 rounding midpoint, or tiny while x and
+// gamma are not zero.
+__device__ __forceinline__ bool rms_flag(float x, float gm, float h) {
+  return near_mid16(h) | (tiny32(h) & (x != 0.0f) & (gm != 0.0f));
+}
+
+// 8 values and their 8 gamma entries -> 8 normalized values (bf16).
+__device__ __forceinline__ uint4 rms8(uint4 xv, uint4 gv, float r32, double r64) {
+  const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+  const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+  float x[8], gm[8], h[8];
+  bool any = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16lo(xw[i]);
+    x[2 * i + 1] = bf16hi(xw[i]);
+    gm[2 * i] = bf16lo(gw[i]);
+    gm[2 * i + 1] = bf16hi(gw[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[i] = x[i] * r32 * gm[i];
+    any |= rms_flag(x[i], gm[i], h[i]);
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pk_bf16(h[2 * i], h[2 * i + 1]);
+  if (__builtin_expect(any, 0)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (rms_flag(x[i], gm[i], h[i])) {
+        const uint32_t b = rms_slow(x[i], gm[i], r64);
+        o[i >> 1] = (i & 1) ? ((o[i >> 1] & 0xFFFFu) | (b << 16)) : ((o[i >> 1] & 0xFFFF0000u) | b);
+      }
+    }
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 __device__ __forceinline__ double chunk_sumsq(uint4 v) {
@@ -155,12 +237,13 @@ __device__ __forceinline__ void quantize_team(const uint4 (&h)[CH], bool row_ok,
   for (int i = 0; i < CH; ++i) m2 = chunk_amax(h[i], m2);
   uint32_t m = m2.x > m2.y ? m2.x : m2.y;
   m = wave_max_u32(m);
-  if (TW > 1) {
+  if (TW > 1) {   // the team's waves meet in red[team * TW ...]
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
-    m = red[0];
+    const uint32_t* tr = red + (threadIdx.x / TEAM) * TW;
+    m = tr[0];
 #pragma unroll
-    for (int w = 1; w < TW; ++w) m = m > red[w] ? m : red[w];
+    for (int w = 1; w < TW; ++w) m = m > tr[w] ? m : tr[w];
   }
   if (!row_ok) return;
   float s, r, p;
@@ -175,10 +258,24 @@ __device__ __forceinline__ void quantize_team(const uint4 (&h)[CH], bool row_ok,
   }
 }
 
-// One team of TW waves per row (TW = 1: four rows per 256-thread block).
+// Stores the team's bf16 h chunks of one row (the unquantized outputs).
 template <int CH, int TW>
-__global__ __launch_bounds__(TW >= 4 ? 64 * TW : 256) void silu_mul_quant_kernel(
-    const uint4* __restrict__ gu, int64_t rows, int64_t I, uint2* __restrict__ q,
+__device__ __forceinline__ void store_team(const uint4 (&h)[CH], bool row_ok, int64_t row,
+                                           int64_t nch, int team_lane, uint4* __restrict__ out) {
+  if (!row_ok) return;
+  uint4* orow = out + row * nch;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int64_t c = (int64_t)i * 64 * TW + team_lane;
+    if (c < nch) orow[c] = h[i];
+  }
+}
+
+// One team of TW waves per row (TW = 1: four rows per 256-thread block).
+// Q: per-token FP8 codes and scales; else the bf16 h row itself.
+template <int CH, int TW, bool Q>
+__global__ __launch_bounds__(TW >= 4 ? 64 * TW : 256) void silu_mul_kernel(
+    const uint4* __restrict__ gu, int64_t rows, int64_t I, void* __restrict__ out,
     float* __restrict__ scale) {
   constexpr int TEAM = 64 * TW;
   constexpr int RPB = TW >= 4 ? 1 : 4 / TW;
@@ -188,20 +285,25 @@ __global__ __launch_bounds__(TW >= 4 ? 64 * TW : 256) void silu_mul_quant_kernel
   const int64_t nch = I >> 3;
   const bool row_ok = row < rows;
   const uint4* gr = gu + (row_ok ? row : 0) * 2 * nch;
-  uint4 h[CH];
+  uint4 gv[CH], uv[CH], h[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int64_t c = (int64_t)i * TEAM + tl;
-    h[i] = (row_ok && c < nch) ? silu_mul8(ld16(gr + c), ld16(gr + nch + c))
-                               : make_uint4(0, 0, 0, 0);
+    gv[i] = ld16_if(gr, c, row_ok && c < nch);
+    uv[i] = ld16_if(gr + nch, c, row_ok && c < nch);
   }
-  quantize_team<CH, TW>(h, row_ok, row, nch, tl, red, q, scale);
+#pragma unroll
+  for (int i = 0; i < CH; ++i) h[i] = silu_mul8(gv[i], uv[i]);   // silu(0) * 0 = +0
+  if (Q)
+    quantize_team<CH, TW>(h, row_ok, row, nch, tl, red, static_cast<uint2*>(out), scale);
+  else
+    store_team<CH, TW>(h, row_ok, row, nch, tl, static_cast<uint4*>(out));
 }
 
-template <int CH, int TW>
-__global__ __launch_bounds__(TW >= 4 ? 64 * TW : 256) void rmsnorm_quant_kernel(
+template <int CH, int TW, bool Q>
+__global__ __launch_bounds__(TW >= 4 ? 64 * TW : 256) void rmsnorm_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ gamma, int64_t rows,
-    int64_t H, double eps, uint2* __restrict__ q, float* __restrict__ scale) {
+    int64_t H, double eps, void* __restrict__ out, float* __restrict__ scale) {
   constexpr int TEAM = 64 * TW;
   constexpr int RPB = TW >= 4 ? 1 : 4 / TW;
   __shared__ uint32_t red[TW >= 4 ? TW : 4];
@@ -211,40 +313,40 @@ __global__ __launch_bounds__(TW >= 4 ? 64 * TW : 256) void rmsnorm_quant_kernel(
   const int64_t nch = H >> 3;
   const bool row_ok = row < rows;
   const uint4* xr = x + (row_ok ? row : 0) * nch;
-  uint4 h[CH];
-  double ss = 0.0;
+  uint4 h[CH], gv[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int64_t c = (int64_t)i * TEAM + tl;
-    h[i] = (row_ok && c < nch) ? ld16(xr + c) : make_uint4(0, 0, 0, 0);
-    ss += chunk_sumsq(h[i]);
+    h[i] = ld16_if(xr, c, row_ok && c < nch);
   }
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int64_t c = (int64_t)i * TEAM + tl;
+    gv[i] = ld16_if(gamma, c, c < nch);
+  }
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) ss += chunk_sumsq(h[i]);
   ss = wave_sum_f64(ss);
   if (TW > 1) {
     if ((tid & 63) == 0) reds[tid >> 6] = ss;
     __syncthreads();
-    ss = reds[0];
+    const double* tr = reds + (tid / TEAM) * TW;
+    ss = tr[0];
 #pragma unroll
-    for (int w = 1; w < TW; ++w) ss += reds[w];   // fixed order
+    for (int w = 1; w < TW; ++w) ss += tr[w];   // fixed order
   }
   const double r64 = 1.0 / sqrt(ss / (double)H + eps);
   const float r32 = (float)r64;
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int64_t c = (int64_t)i * TEAM + tl;
-    if (row_ok && c < nch) {
-      const uint4 gv = ld16(gamma + c);
-      const uint32_t xw[4] = {h[i].x, h[i].y, h[i].z, h[i].w};
-      const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-      uint32_t o[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        o[k] = rms1(bf16lo(xw[k]), bf16lo(gw[k]), r32, r64) |
-               (rms1(bf16hi(xw[k]), bf16hi(gw[k]), r32, r64) << 16);
-      h[i] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
+    if (row_ok && c < nch) h[i] = rms8(h[i], gv[i], r32, r64);
   }
-  quantize_team<CH, TW>(h, row_ok, row, nch, tl, red, q, scale);
+  if (Q)
+    quantize_team<CH, TW>(h, row_ok, row, nch, tl, red, static_cast<uint2*>(out), scale);
+  else
+    store_team<CH, TW>(h, row_ok, row, nch, tl, static_cast<uint4*>(out));
 }
 
 // ---- static calibration: exact order statistics by two radix passes -------
@@ -355,16 +457,21 @@ __device__ __forceinline__ uint2 quant8_sat(uint4 raw, float s, float r, float p
   lo = __builtin_amdgcn_cvt_pk_fp8_f32(yc[2], yc[3], lo, true);
   uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(yc[4], yc[5], 0, false);
   hi = __builtin_amdgcn_cvt_pk_fp8_f32(yc[6], yc[7], hi, true);
-  const float sp = PRE ? s * p : s;
+  bool any = false;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (needs_fixup(y[i])) {
-      uint32_t& word = (i < 4) ? lo : hi;
-      const int sh = 8 * (i & 3);
-      const float ax = __builtin_fabsf(PRE ? x[i] * p : x[i]);
-      const uint32_t mag = exact_mag(ax, sp, __builtin_fabsf(y[i]));
-      const uint32_t code = mag | ((__float_as_uint(x[i]) >> 24) & 0x80u);
-      word = (word & ~(0xFFu << sh)) | (code << sh);
+  for (int i = 0; i < 8; ++i) any |= needs_fixup(y[i]);
+  if (__builtin_expect(any, 0)) {
+    const float sp = PRE ? s * p : s;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (needs_fixup(y[i])) {
+        uint32_t& word = (i < 4) ? lo : hi;
+        const int sh = 8 * (i & 3);
+        const float ax = __builtin_fabsf(PRE ? x[i] * p : x[i]);
+        const uint32_t mag = exact_mag(ax, sp, __builtin_fabsf(y[i]));
+        const uint32_t code = mag | ((__float_as_uint(x[i]) >> 24) & 0x80u);
+        word = (word & ~(0xFFu << sh)) | (code << sh);
+      }
     }
   }
   return make_uint2(lo, hi);
@@ -400,13 +507,14 @@ __global__ __launch_bounds__(TW >= 4 ? 64 * TW : 256) void kv_quant_kernel(
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int64_t c = (int64_t)i * TEAM + tl;
-    h[i] = (row_ok && c < nch) ? ld16(xr + c) : make_uint4(0, 0, 0, 0);
+    h[i] = ld16_if(xr, c, row_ok && c < nch);
   }
   quantize_team<CH, TW>(h, row_ok, row_ok ? slot : 0, nch, tl, red, cache, cscale);
 }
 
-// Row-team launch ladder shared by the row kernels: TW = 1 for rows of up to
-// 512 chunks (4096 values), else 4 waves, then 16; CH chunks per lane.
+// Row-team launch ladders: CH chunks per lane, TW waves per row. The wide
+// ladder starts at teams of 4 waves (one row per block), with CH the fewest
+// chunks per lane that cover the row, so no lane of a 14336-wide row idles.
 template <template <int, int> class Launch, typename... A>
 int launch_ladder(int64_t nch, A... a) {
   if (nch <= 64) { Launch<1, 1>::go(a...); return 0; }
@@ -414,6 +522,21 @@ int launch_ladder(int64_t nch, A... a) {
   if (nch <= 256) { Launch<4, 1>::go(a...); return 0; }
   if (nch <= 512) { Launch<8, 1>::go(a...); return 0; }
   if (nch <= 1024) { Launch<4, 4>::go(a...); return 0; }
+  if (nch <= 2048) { Launch<8, 4>::go(a...); return 0; }
+  if (nch <= 4096) { Launch<4, 16>::go(a...); return 0; }
+  if (nch <= 8192) { Launch<8, 16>::go(a...); return 0; }
+  return -1;
+}
+
+template <template <int, int> class Launch, typename... A>
+int launch_ladder_wide(int64_t nch, A... a) {
+  if (nch <= 256) { Launch<1, 4>::go(a...); return 0; }
+  if (nch <= 512) { Launch<2, 4>::go(a...); return 0; }
+  if (nch <= 768) { Launch<3, 4>::go(a...); return 0; }
+  if (nch <= 1024) { Launch<4, 4>::go(a...); return 0; }
+  if (nch <= 1280) { Launch<5, 4>::go(a...); return 0; }
+  if (nch <= 1536) { Launch<6, 4>::go(a...); return 0; }
+  if (nch <= 1792) { Launch<7, 4>::go(a...); return 0; }
   if (nch <= 2048) { Launch<8, 4>::go(a...); return 0; }
   if (nch <= 4096) { Launch<4, 16>::go(a...); return 0; }
   if (nch <= 8192) { Launch<8, 16>::go(a...); return 0; }
@@ -429,22 +552,29 @@ struct RowsGrid {
   static dim3 threads() { return dim3(TW >= 4 ? 64 * TW : 256); }
 };
 
-template <int CH, int TW>
+template <bool Q>
 struct SiluLaunch {
-  static void go(const void* gu, int64_t rows, int64_t I, uint8_t* q, float* s, hipStream_t st) {
-    hipLaunchKernelGGL((silu_mul_quant_kernel<CH, TW>), (RowsGrid<CH, TW>::blocks(rows)),
-                       (RowsGrid<CH, TW>::threads()), 0, st, (const uint4*)gu, rows, I,
-                       (uint2*)q, s);
-  }
+  template <int CH, int TW>
+  struct L {
+    static void go(const void* gu, int64_t rows, int64_t I, void* out, float* s,
+                   hipStream_t st) {
+      hipLaunchKernelGGL((silu_mul_kernel<CH, TW, Q>), (RowsGrid<CH, TW>::blocks(rows)),
+                         (RowsGrid<CH, TW>::threads()), 0, st, (const uint4*)gu, rows, I, out,
+                         s);
+    }
+  };
 };
-template <int CH, int TW>
+template <bool Q>
 struct RmsLaunch {
-  static void go(const void* x, const void* g, int64_t rows, int64_t H, double eps,
-                 uint8_t* q, float* s, hipStream_t st) {
-    hipLaunchKernelGGL((rmsnorm_quant_kernel<CH, TW>), (RowsGrid<CH, TW>::blocks(rows)),
-                       (RowsGrid<CH, TW>::threads()), 0, st, (const uint4*)x,
-                       (const uint4*)g, rows, H, eps, (uint2*)q, s);
-  }
+  template <int CH, int TW>
+  struct L {
+    static void go(const void* x, const void* g, int64_t rows, int64_t H, double eps,
+                   void* out, float* s, hipStream_t st) {
+      hipLaunchKernelGGL((rmsnorm_kernel<CH, TW, Q>), (RowsGrid<CH, TW>::blocks(rows)),
+                         (RowsGrid<CH, TW>::threads()), 0, st, (const uint4*)x,
+                         (const uint4*)g, rows, H, eps, out, s);
+    }
+  };
 };
 template <int CH, int TW>
 struct KvLaunch {
@@ -460,12 +590,25 @@ struct KvLaunch {
 
 int launch_silu_mul_quant(const void* gu, int64_t rows, int64_t I, uint8_t* q,
                           float* scale, hipStream_t st) {
-  return launch_ladder<SiluLaunch>(I / 8, gu, rows, I, q, scale, st);
+  return launch_ladder_wide<SiluLaunch<true>::template L>(I / 8, gu, rows, I, (void*)q,
+                                                          scale, st);
+}
+
+int launch_silu_mul(const void* gu, int64_t rows, int64_t I, void* h, hipStream_t st) {
+  return launch_ladder_wide<SiluLaunch<false>::template L>(I / 8, gu, rows, I, h,
+                                                           (float*)nullptr, st);
 }
 
 int launch_rmsnorm_quant(const void* x, const void* gamma, int64_t rows, int64_t H,
                          double eps, uint8_t* q, float* scale, hipStream_t st) {
-  return launch_ladder<RmsLaunch>(H / 8, x, gamma, rows, H, eps, q, scale, st);
+  return launch_ladder_wide<RmsLaunch<true>::template L>(H / 8, x, gamma, rows, H, eps,
+                                                         (void*)q, scale, st);
+}
+
+int launch_rmsnorm(const void* x, const void* gamma, int64_t rows, int64_t H, double eps,
+                   void* h, hipStream_t st) {
+  return launch_ladder_wide<RmsLaunch<false>::template L>(H / 8, x, gamma, rows, H, eps, h,
+                                                          (float*)nullptr, st);
 }
 
 int launch_kv_quant(const void* x, int64_t T, int64_t width, const int64_t* slots,

@@ -43,6 +43,9 @@ int launch_silu_mul_quant(const void* gu, int64_t rows, int64_t I, uint8_t* q,
                           float* scale, hipStream_t st);
 int launch_rmsnorm_quant(const void* x, const void* gamma, int64_t rows, int64_t H,
                          double eps, uint8_t* q, float* scale, hipStream_t st);
+int launch_silu_mul(const void* gu, int64_t rows, int64_t I, void* h, hipStream_t st);
+int launch_rmsnorm(const void* x, const void* gamma, int64_t rows, int64_t H, double eps,
+                   void* h, hipStream_t st);
 int launch_kv_quant(const void* x, int64_t T, int64_t width, const int64_t* slots,
                     int64_t n_slots, uint8_t* cache, float* cscale, hipStream_t st);
 size_t calib_workspace_bytes();

@@ -60,25 +60,23 @@ __global__ __launch_bounds__(TEAM_WAVES >= 4 ? 64 * TEAM_WAVES : 256) void quant
   const uint4* xr = x + (row_ok ? row : 0) * nch;
 
   uint4 v[CH];
-  us2 m2 = {0, 0};
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int64_t c = (int64_t)i * TEAM + tl;
-    if (row_ok && c < nch) {
-      v[i] = ld16_nt(xr + c);
-    } else {
-      v[i] = make_uint4(0, 0, 0, 0);
-    }
-    m2 = chunk_amax(v[i], m2);
+    v[i] = ld16_if<true>(xr, c, row_ok && c < nch);
   }
+  us2 m2 = {0, 0};
+#pragma unroll
+  for (int i = 0; i < CH; ++i) m2 = chunk_amax(v[i], m2);
   uint32_t m = m2.x > m2.y ? m2.x : m2.y;
   m = wave_max_u32(m);
-  if (TEAM_WAVES > 1) {
+  if (TEAM_WAVES > 1) {   // the team's waves meet in red[team * TEAM_WAVES ...]
     if ((tid & 63) == 0) red[tid >> 6] = m;
     __syncthreads();
-    m = red[0];
+    const uint32_t* tr = red + team * TEAM_WAVES;
+    m = tr[0];
 #pragma unroll
-    for (int w = 1; w < TEAM_WAVES; ++w) m = m > red[w] ? m : red[w];
+    for (int w = 1; w < TEAM_WAVES; ++w) m = m > tr[w] ? m : tr[w];
   }
   if (!row_ok) return;
   float s, r, p;

@@ -71,16 +71,22 @@ __device__ __forceinline__ uint2 quant8(uint4 raw, float s, float r, float p) {
   lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
   uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
   hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
-  const float sp = PRE ? s * p : s;
+  // the 8 tests without a branch, then one branch for the chunk
+  bool any = false;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (needs_fixup(y[i])) {
-      uint32_t& word = (i < 4) ? lo : hi;
-      const int sh = 8 * (i & 3);
-      float ax = __builtin_fabsf(PRE ? x[i] * p : x[i]);
-      uint32_t mag = exact_mag(ax, sp, __builtin_fabsf(y[i]));
-      uint32_t code = mag | ((__float_as_uint(x[i]) >> 24) & 0x80u);
-      word = (word & ~(0xFFu << sh)) | (code << sh);
+  for (int i = 0; i < 8; ++i) any |= needs_fixup(y[i]);
+  if (__builtin_expect(any, 0)) {
+    const float sp = PRE ? s * p : s;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (needs_fixup(y[i])) {
+        uint32_t& word = (i < 4) ? lo : hi;
+        const int sh = 8 * (i & 3);
+        float ax = __builtin_fabsf(PRE ? x[i] * p : x[i]);
+        uint32_t mag = exact_mag(ax, sp, __builtin_fabsf(y[i]));
+        uint32_t code = mag | ((__float_as_uint(x[i]) >> 24) & 0x80u);
+        word = (word & ~(0xFFu << sh)) | (code << sh);
+      }
     }
   }
   return make_uint2(lo, hi);

@@ -195,6 +195,20 @@ int fp8_rmsnorm_quant(const void* x_bf16, const void* gamma_bf16, int64_t rows, 
                       double eps, uint8_t* q, float* scale, void* stream);
 
 /*
+ * fp8_silu_mul, fp8_rmsnorm -- the same two producers with the bf16 h row as
+ * the output instead of its FP8 codes: h_bf16 [rows, I] (resp. [rows, H]),
+ * bit-identical to the h the quantizing entry points quantize. The norm in
+ * bf16 is what feeds layers that stay in bf16 (the final norm before
+ * lm_head, which the FP8 schemes leave unquantized: the Llama-3.1-8B-
+ * Instruct-FP8-Dynamic page's model description). Same size rules, errors
+ * and stream semantics as fp8_silu_mul_quant / fp8_rmsnorm_quant;
+ * h_bf16 16-byte aligned.
+ */
+int fp8_silu_mul(const void* gu_bf16, int64_t rows, int64_t I, void* h_bf16, void* stream);
+int fp8_rmsnorm(const void* x_bf16, const void* gamma_bf16, int64_t rows, int64_t H, double eps,
+                void* h_bf16, void* stream);
+
+/*
  * fp8_calib_scale -- static per-tensor scale from percentile calibration:
  *   amax = max(|x_(k_lo)|, |x_(k_hi)|), k = ceil(p * n) clamped to [1, n]
  *   (nearest-rank order statistics of the n values, p = permille / 1000),

@@ -366,7 +366,12 @@ def silu_mul_bf16(gu_bits: np.ndarray) -> np.ndarray:
         if b is None:
             side = -1 if hv > 0 else 1   # unreachable for near-midpoint values
         else:
-            d = a - b
+            if b == 0 and m != 0:
+                # e^-g below the decimal range (g > 2.3e6): m * e^-g is not
+                # zero but smaller than any nonzero a, and has the sign of m
+                d = a if a != 0 else -m
+            else:
+                d = a - b
             side = (d > 0) - (d < 0)     # sign of h - m
         up = side * (1 if hv > 0 else -1)            # sign of |h| - |m|
         if up > 0 or (up == 0 and (lo_bits & 1)):

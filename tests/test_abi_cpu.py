@@ -122,6 +122,18 @@ def test_fused_producer_errors(L):
     assert g(A, A, 4, 256, float("nan"), A, A, None) == -2
     assert g(A, MIS, 4, 256, 1e-5, A, A, None) == -3
     assert g(None, None, 0, 256, 1e-5, None, None, None) == 0
+    f = L.fp8_silu_mul
+    assert f(None, 4, 256, A, None) == -1
+    assert f(A, 4, 100, A, None) == -2
+    assert f(A, 4, 65536 + 8, A, None) == -2
+    assert f(A, 4, 256, MIS, None) == -3
+    assert f(None, 0, 256, None, None) == 0
+    g = L.fp8_rmsnorm
+    assert g(A, A, 4, 256, 1e-5, None, None) == -1
+    assert g(A, A, 4, 12, 1e-5, A, None) == -2
+    assert g(A, A, 4, 256, -1.0, A, None) == -2
+    assert g(A, A, 4, 256, 1e-5, MIS, None) == -3
+    assert g(None, None, 0, 256, 1e-5, None, None) == 0
 
 
 def test_calibration_and_static_errors(L):

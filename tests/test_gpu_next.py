@@ -245,3 +245,96 @@ def test_silu_exact_ties_round_toward_zero(F):
     qo, so = O.silu_mul_quant(gu)
     assert_scales_equal(s.cpu().numpy(), so, "tie scales")
     assert_codes_equal(q.cpu().numpy(), qo, "tie codes")
+
+
+@pytest.mark.parametrize("rows,inner", SILU_SHAPES)
+def test_silu_mul_bf16(F, rows, inner):
+    """The bf16 h itself, bit-exact (its rounding is otherwise seen only
+    through the FP8 codes, which hide most one-ulp differences)."""
+    say(f"silu_mul bf16 {rows}x{inner}")
+    gu = gate_up(rows, inner, 5100 + inner)
+    h = F.fp8_silu_mul(dev_bf16(gu))
+    torch.cuda.synchronize()
+    got = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    want = O.silu_mul_bf16(gu)
+    bad = np.flatnonzero(got.ravel() != want.ravel())
+    assert bad.size == 0, f"{bad.size} h mismatches, first at {bad[:5]}"
+
+
+def every_bf16_gate(seed, rows):
+    """Rows [rows, 2I] holding every finite bf16 g once per row, each with its
+    own random u in [-1, 1] (so h stays finite)."""
+    b = np.arange(65536, dtype=np.uint32)
+    finite = (b & 0x7F80) != 0x7F80
+    g = b[finite].astype(np.uint16)
+    pad = (-g.size) % 8
+    g = np.concatenate([g, np.zeros(pad, np.uint16)])
+    rng = np.random.default_rng(seed)
+    u = bits_of(rng.uniform(-1.0, 1.0, (rows, g.size)))
+    return np.concatenate([np.broadcast_to(g, (rows, g.size)), u], axis=1).astype(np.uint16)
+
+
+def test_silu_mul_bf16_every_gate(F):
+    """All finite bf16 gate values, in the fast path's range (|g| <= 64) and
+    beyond, against the oracle bit for bit."""
+    gu = every_bf16_gate(41, 4)
+    say(f"silu_mul bf16 every gate {gu.shape}")
+    h = F.fp8_silu_mul(dev_bf16(gu))
+    torch.cuda.synchronize()
+    got = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    want = O.silu_mul_bf16(gu)
+    bad = np.flatnonzero(got.ravel() != want.ravel())
+    assert bad.size == 0, f"{bad.size} h mismatches, first at {bad[:5]}"
+
+
+@pytest.mark.parametrize("rows,hidden", RMS_SHAPES)
+def test_rmsnorm_bf16(F, rows, hidden):
+    say(f"rmsnorm bf16 {rows}x{hidden}")
+    x, gamma = norm_input(rows, hidden, 6100 + hidden)
+    h = F.fp8_rmsnorm(dev_bf16(x), dev_bf16(gamma))
+    torch.cuda.synchronize()
+    got = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    want = O.rmsnorm_bf16(x, gamma)
+    bad = np.flatnonzero(got.ravel() != want.ravel())
+    assert bad.size == 0, f"{bad.size} h mismatches, first at {bad[:5]}"
+
+
+def test_bf16_and_fp8_outputs_agree(F):
+    """The quantizing entry points quantize exactly the h the bf16 ones give."""
+    gu = gate_up(33, 1536, 91)
+    h = F.fp8_silu_mul(dev_bf16(gu))
+    q1, s1 = F.fp8_silu_mul_quant(dev_bf16(gu))
+    q2, s2 = F.fp8_quant_act(h)
+    x, gamma = norm_input(33, 2048, 92)
+    hn = F.fp8_rmsnorm(dev_bf16(x), dev_bf16(gamma))
+    q3, s3 = F.fp8_rmsnorm_quant(dev_bf16(x), dev_bf16(gamma))
+    q4, s4 = F.fp8_quant_act(hn)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(s1, s2)
+    assert torch.equal(q3, q4) and torch.equal(s3, s4)
+
+
+def test_silu_structural_ties(F):
+    """g*u/2 an exact midpoint with tiny g (the true h is above it for g > 0,
+    below for g < 0), and g*u one with huge g (below it): bf16 h and codes."""
+    U = np.arange(87, 171, 2, dtype=np.float64)
+    gs, us = [], []
+    for g, scale in ((3.0 * 2.0 ** -102, 1.0), (-3.0 * 2.0 ** -102, 1.0),
+                     (3.0 * 2.0 ** -60, 1.0), (3.0 * 2.0 ** 98, 2.0 ** -30),
+                     (3.0 * 2.0 ** 40, 2.0 ** -30)):
+        for sgn in (1.0, -1.0):
+            gs += [g] * U.size
+            us += list(sgn * U * scale)
+    n = len(gs)
+    pad = (-n) % 8
+    gu = bits_of(np.concatenate([gs, [1.0] * pad, us, [1.0] * pad]))[None, :]
+    h = F.fp8_silu_mul(dev_bf16(gu))
+    q, s = F.fp8_silu_mul_quant(dev_bf16(gu))
+    torch.cuda.synchronize()
+    got = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    want = O.silu_mul_bf16(gu)
+    bad = np.flatnonzero(got.ravel() != want.ravel())
+    assert bad.size == 0, f"{bad.size} h mismatches, first at {bad[:5]}"
+    qo, so = O.silu_mul_quant(gu)
+    assert_scales_equal(s.cpu().numpy(), so, "structural tie scales")
+    assert_codes_equal(q.cpu().numpy(), qo, "structural tie codes")

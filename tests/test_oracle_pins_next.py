@@ -138,6 +138,26 @@ def check_silu_identities(o):
     assert np.all(np.abs((hp - hn) - gs) <= 2.0 ** -7 * (np.abs(hp) + np.abs(hn)) + 1e-30)
 
 
+def check_silu_structural_ties(o):
+    """g*u (huge g) or g*u/2 (tiny g) an exact bf16 midpoint. silu(g) < g for
+    g > 0 puts |h| below the tie for huge g; silu(g) = g/2 + g^2/4 + ... puts
+    it above for tiny g > 0 and below for tiny g < 0. The bf16 neighbour
+    toward zero is the truncation of the midpoint's value."""
+    U = np.arange(87, 171, 2, dtype=np.float64)          # 3 * U: odd, 9 bits
+    trunc = lambda v: (np.asarray(v, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    for g, halve, away in ((3.0 * 2.0 ** 98, False, False), (3.0 * 2.0 ** 120, False, False),
+                           (3.0 * 2.0 ** -102, True, True), (-3.0 * 2.0 ** -102, True, False)):
+        for sgn in (1.0, -1.0):
+            u = sgn * U * (2.0 ** -30 if not halve else 1.0)
+            m = g * u / (2.0 if halve else 1.0)
+            gu = bits_of(np.concatenate([np.full(U.size, g), u]))[None, :]
+            assert np.array_equal(o.bf16_to_f64(gu[0, U.size:]), u)
+            got = o.silu_mul_bf16(gu)[0]
+            lo = trunc(m)
+            want = lo + 1 if away else lo
+            assert np.array_equal(got, want.astype(np.uint16)), (g, sgn, got, want)
+
+
 def check_rmsnorm_highprec(o):
     rng = np.random.default_rng(24)
     rows = [rng.standard_normal(48), rng.standard_normal(48) * 1e-3,   # eps matters
@@ -232,6 +252,7 @@ def check_kv_scatter(o):
 
 
 CHECKS = [check_bf16_rounding, check_silu_mul_highprec, check_silu_identities,
+          check_silu_structural_ties,
           check_rmsnorm_highprec, check_rmsnorm_special, check_nearest_rank_bruteforce,
           check_static_quant, check_kv_scatter]
 
