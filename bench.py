@@ -18,6 +18,8 @@ Also reported:
   decode        the Llama-3.1-70B decode linears at M in {1, 8, 32, 64}:
                 end-to-end fp8_linear weight GB/s with cold weights
                 (rotated copies well beyond the 256 MB last-level cache);
+  block         the block variant on the Llama-3.2-3B linears at M = 8192:
+                group-128 quantizer and block-scaled GEMM times, TFLOP/s;
   next_rows     SwiGLU->FP8 and RMSNorm->FP8 fused quantizers, percentile
                 calibration over a 512 x 2048-token set, static quantization
                 and the FP8 KV-cache write, in GB/s of algorithmic bytes;
@@ -338,6 +340,44 @@ def bench_next_rows(F, torch):
     return out
 
 
+def bench_block(F, torch):
+    """Block variant on the Llama-3.2-3B shapes, M = 8192 tokens: group-128
+    activation quantization and the block-scaled GEMM, each timed alone
+    (median of batches of back-to-back launches, HIP events)."""
+    import synth
+    out = {}
+    tot_flops = tot_us = 0.0
+    M = synth.M_OF["c4"][0]
+    for j, (name, K, N) in enumerate(synth.SHAPES["c4"]):
+        log(f"block setup: {name} {K}->{N}, M={M}")
+        d = synth.workload(4, j)
+        x = to_dev(d["x"], torch)
+        w = to_dev(d["w"], torch)
+        qw, sw = F.fp8_quant_weight_block(w)
+        del w
+        qx = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+        sx = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        q_us = _time_us(torch, lambda: F.fp8_quant_act(x, group=128, q=qx, scale=sx))
+        g_us = _time_us(torch, lambda: F.fp8_gemm_block(qx, sx, qw, sw, y=y))
+        fl = 2 * M * N * K
+        tot_flops += fl
+        tot_us += q_us + g_us
+        tf = fl / (g_us * 1e-6) / 1e12
+        qbytes = 3 * M * K + 4 * M * (K // 128)
+        out[name] = {"gemm_us": round(g_us, 2), "gemm_tflops": round(tf, 1),
+                     "frac": round(tf / PEAK_FP8_TFLOPS, 4), "quant_us": round(q_us, 2),
+                     "quant_gbs": round(qbytes / (q_us * 1e-6) / 1e9, 1)}
+        log(f"  {name}: GEMM {g_us:.1f} us ({tf:.0f} TFLOP/s), group quant {q_us:.1f} us")
+        del x, qx, sx, y, qw, sw
+        torch.cuda.empty_cache()
+    out["linear_tflops"] = round(tot_flops / (tot_us * 1e-6) / 1e12, 1)
+    out["protocol"] = ("fp8_quant_act(group 128) and fp8_gemm_block timed separately; "
+                       "median of 5 batches of 20 launches; linear_tflops = all four "
+                       "linears' flops over the sum of both times")
+    return out
+
+
 def copy_calibration(torch):
     src = torch.randint(0, 255, (COPY_BYTES,), dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -390,6 +430,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-regime section")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the block-variant section (Llama-3.2-3B shapes)")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the fused-producer / calibration / KV-cache section")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -403,7 +445,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this benchmark runs on one GPU only (got --gpus {args.gpus}, "
-              f"WORLD_SIZE {world}); multi-GPU scaling is not part of this build.",
+              f"WORLD_SIZE {world}); the path is measured on one GPU only.",
               file=sys.stderr)
         sys.exit(2)
 
@@ -458,6 +500,8 @@ def main():
     }
     if not args.no_decode:
         out["decode"] = bench_decode(F, torch)
+    if not args.no_block:
+        out["block"] = bench_block(F, torch)
     if not args.no_next:
         log("fused producers, calibration, KV cache ...")
         out["next_rows"] = bench_next_rows(F, torch)
