@@ -12,7 +12,8 @@
 //    128-byte K steps of those rows (wave w: steps w, w+4, ...), so the
 //    workgroup streams contiguous K and no two waves load the same bytes;
 //  * each wave keeps D K-steps of fragments in flight (loads for step t+D
-//    issue right after step t's MFMAs), weight loads are non-temporal;
+//    issue right after step t's MFMAs); weight loads are plain loads
+//    (non-temporal hints measured slower);
 //  * MFMA operand A = 16 weight rows, B = 16 token rows (M padded by
 //    clamping the row index; the padded outputs are dropped);
 //  * the 4 waves' partial sums are added in a fixed order through LDS;
