@@ -366,18 +366,33 @@ __global__ __launch_bounds__(256, WPC) void gemm_prefill_deep_kernel(
   // the end the last step is loaded again into a slot that is never read,
   // which keeps the number of loads in flight (and so every wait count)
   // constant.
-  auto issue_one = [&](int kt, int q) {
+  auto issue_at = [&](uint32_t slot, int kt, int q) {
     const bool isx = q < DXQ;
-    const uint32_t sb = lds0 + (uint32_t)((kt % S) * STAGE) + (isx ? 0 : XB) +
-                        ((isx ? q : q - DXQ) * 4 + wave) * 1024;
+    const uint32_t sb = lds0 + slot + (isx ? 0 : XB) + ((isx ? q : q - DXQ) * 4 + wave) * 1024;
     const uint8_t* base = (isx ? qx : qw) + (size_t)min(kt, KT - 1) * DBK;
     dma16(base, goff[q], sb);
   };
+  // byte offsets of the slot step kt+1 is read from and of the slot step
+  // kt+S-1 is loaded into, advanced by one slot per step (no division)
+  uint32_t rslot = (uint32_t)STAGE, wslot = (uint32_t)((S - 1) * STAGE);
   const int arow0 = wn * DTN + lr, brow0 = wm * DTM + lr;
   // one 16-byte half (h = 0: chunk 2*kh, 1: chunk 2*kh+1) of a fragment
-  auto rd_half = [&](v8i& f, const uint8_t* base, int row, int h) {
-    const uint4 v = *reinterpret_cast<const uint4*>(base + dlds_off(row, 2 * kh + h));
+  // Fragment f of a step sits at a per-lane base + 2048 * f: rows 32 apart
+  // share their low 5 bits, so the in-group permutation is the same. One
+  // address add per operand half and step; the rest are immediate offsets.
+  const uint32_t oA0 = XB + dlds_off(arow0, 2 * kh), oA1 = XB + dlds_off(arow0, 2 * kh + 1);
+  const uint32_t oB0 = dlds_off(brow0, 2 * kh), oB1 = dlds_off(brow0, 2 * kh + 1);
+  auto rd_at = [&](v8i& f, const uint8_t* p, int h) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
     f[4 * h + 0] = v.x; f[4 * h + 1] = v.y; f[4 * h + 2] = v.z; f[4 * h + 3] = v.w;
+  };
+  // Read order of a step's fragments: A0, B0 .. B(DMJ-1), A1 .. A(DNI-1),
+  // the order in which the next step's MFMAs first use them, so that every
+  // fragment has many MFMAs between its read and its use.
+  auto frag_of = [](int o) { return o == 0 ? 0 : (o <= DMJ ? DNI + o - 1 : o - DMJ); };
+  auto read_frag = [&](v8i (&Af)[DNI], v8i (&Bf)[DMJ], uint32_t slot, int f, int h) {
+    if (f < DNI) rd_at(Af[f], smem + slot + (h ? oA1 : oA0) + 2048 * f, h);
+    else rd_at(Bf[f - DNI], smem + slot + (h ? oB1 : oB0) + 2048 * (f - DNI), h);
   };
 
   v16f acc[DNI][DMJ];
@@ -401,21 +416,13 @@ __global__ __launch_bounds__(256, WPC) void gemm_prefill_deep_kernel(
       if (((s - (S - 1)) & 1) == 0) issue_sx((s - (S - 1)) / 2 + 2);
     }
 #pragma unroll
-    for (int q = 0; q < DLPS; ++q) issue_one(s, q);
+    for (int q = 0; q < DLPS; ++q) issue_at((uint32_t)(s * STAGE), s, q);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * DLPS));
   __syncthreads();
   v8i A[2][DNI], B[2][DMJ];
 #pragma unroll
-  for (int i = 0; i < DNI; ++i) {
-    rd_half(A[0][i], smem + XB, arow0 + 32 * i, 0);
-    rd_half(A[0][i], smem + XB, arow0 + 32 * i, 1);
-  }
-#pragma unroll
-  for (int j = 0; j < DMJ; ++j) {
-    rd_half(B[0][j], smem, brow0 + 32 * j, 0);
-    rd_half(B[0][j], smem, brow0 + 32 * j, 1);
-  }
+  for (int r = 0; r < 2 * (DNI + DMJ); ++r) read_frag(A[0], B[0], 0u, frag_of(r >> 1), r & 1);
 
   // Step kt: wait until step kt+1 has landed (S-3 newer steps may still be
   // in flight), publish it with the barrier (which also frees the slot step
@@ -430,6 +437,15 @@ __global__ __launch_bounds__(256, WPC) void gemm_prefill_deep_kernel(
   // loads issued after step kt+1's: S-3 steps, plus (block) one scale load
   // for every even step among them
   constexpr int WAITN = (S - 3) * DLPS + (BLOCK ? (S - 3) / 2 : 0);
+  // Per-channel variant (S = 5): the loads go out in pairs on odd steps kt,
+  // for steps kt+3 and kt+4, each 16-row group's two 64-byte halves of the
+  // same 128-byte lines back to back, so that the second request of a line
+  // meets the first one in flight instead of fetching the line again. Wait
+  // counts: at even kt the pair issued at kt-1 (2*DLPS loads) may still be
+  // in flight; at odd kt only the last load of the pair holding kt+1.
+  constexpr bool PAIRED = !BLOCK && S == 5;
+  constexpr int WAIT_EVEN = PAIRED ? 2 * DLPS : WAITN;
+  constexpr int WAIT_ODD = PAIRED ? 1 : WAITN;
   // block variant: factor of group g for this lane's rows, and the rescale
   // of the accumulator from the previous factor to it
   auto group_rescale = [&](int g, float (&rho)[DMJ]) {
@@ -447,11 +463,13 @@ __global__ __launch_bounds__(256, WPC) void gemm_prefill_deep_kernel(
     constexpr int cur = decltype(cur_c)::value;
     constexpr bool more = decltype(more_c)::value;
     if (more) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(WAITN));
-      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(cur == 0 ? WAIT_EVEN : WAIT_ODD));
+      // A bare barrier: the LDS data is published by each wave's own vmcnt
+      // wait, and every wave has waited (lgkmcnt) for its reads of the slot
+      // about to be refilled before the MFMAs that used them, so the
+      // lgkmcnt(0) of __syncthreads() would only stall the matrix core.
+      asm volatile("s_barrier" ::: "memory");
     }
-    const uint8_t* nX = smem + ((kt + 1) % S) * STAGE;
-    const uint8_t* nW = nX + XB;
     // block variant, first stage of group g = kt/2: rescale to f_g
     float rho[DMJ];
     if constexpr (BLOCK && cur == 0) {
@@ -464,13 +482,17 @@ __global__ __launch_bounds__(256, WPC) void gemm_prefill_deep_kernel(
 #pragma unroll
         for (int u = 0; u < RPM; ++u) {
           const int r = t * RPM + u;
-          if (r < NR) {
-            const int f = r >> 1, h = r & 1;
-            if (f < DNI) rd_half(A[cur ^ 1][f], nW, arow0 + 32 * f, h);
-            else rd_half(B[cur ^ 1][f - DNI], nX, brow0 + 32 * (f - DNI), h);
-          }
+          if (r < NR) read_frag(A[cur ^ 1], B[cur ^ 1], rslot, frag_of(r >> 1), r & 1);
         }
-        if (t < DLPS) issue_one(kt + S - 1, t);
+        if constexpr (PAIRED) {
+          if (cur == 1 && t < 2 * DLPS) {
+            const uint32_t ws3 = wslot == 0u ? (uint32_t)((S - 1) * STAGE) : wslot - STAGE;
+            if ((t & 1) == 0) issue_at(ws3, kt + 3, t >> 1);
+            else issue_at(wslot, kt + 4, t >> 1);
+          }
+        } else {
+          if (t < DLPS) issue_at(wslot, kt + S - 1, t);
+        }
       }
       const int i = t / DMJ, j = t % DMJ;
       if constexpr (BLOCK && cur == 0) {
@@ -480,12 +502,21 @@ __global__ __launch_bounds__(256, WPC) void gemm_prefill_deep_kernel(
       acc[i][j] = mfma_e4m3_32x32x64(A[cur][i], B[cur][j], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    rslot = rslot + STAGE == (uint32_t)(S * STAGE) ? 0u : rslot + STAGE;
+    wslot = wslot + STAGE == (uint32_t)(S * STAGE) ? 0u : wslot + STAGE;
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  for (int kt = 0; kt < KT - 2; kt += 2) {
-    step(kt, I0(), std::true_type());
-    step(kt + 1, I1(), std::true_type());
+  // The first two steps are peeled: the loop is then entered only from code
+  // identical to its own back edge, and the compiler keeps its LDS waits at
+  // the loop head partial instead of draining every read.
+  if (KT >= 4) {
+    step(0, I0(), std::true_type());
+    step(1, I1(), std::true_type());
+    for (int kt = 2; kt < KT - 2; kt += 2) {
+      step(kt, I0(), std::true_type());
+      step(kt + 1, I1(), std::true_type());
+    }
   }
   step(KT - 2, I0(), std::true_type());
   step(KT - 1, I1(), std::false_type());
@@ -497,33 +528,43 @@ __global__ __launch_bounds__(256, WPC) void gemm_prefill_deep_kernel(
   // DEPI bytes: 8-byte writes from 32 consecutive rows fall on distinct
   // banks), then stores it row-wise, 16 bytes per lane: every store
   // instruction covers whole 256-byte row segments.
+  // The per-channel epilogue's scales: one sx row and one sw column per
+  // thread, loaded here (their latency overlaps the drain above and the
+  // barrier below), then shared through LDS past the staging area; a global
+  // load per column group with a wait after each would cost a memory round
+  // trip each.
+  constexpr int SCL = 4 * DTM * EPI;   // byte offset of the scale area
+  static_assert(SCL + 4 * (BM + BN) <= RING, "scale area inside the ring");
+  float sxv = 0.f, swv = 0.f;
+  if constexpr (!BLOCK) {
+    sxv = sx[min(m0 + tid, M - 1)];
+    if (tid < BN) swv = sw[min(n0 + tid, N - 1)];
+  }
   __syncthreads();  // every wave is done reading the ring
+  float* scl = reinterpret_cast<float*>(smem + SCL);   // sx [BM] then sw [BN]
+  if constexpr (!BLOCK) {
+    scl[tid] = sxv;
+    if (tid < BN) scl[BM + tid] = swv;
+    __syncthreads();
+  }
   uint8_t* ep = smem + wave * (DTM * EPI);
 #pragma unroll
   for (int j = 0; j < DMJ; ++j) {
     const int ml = 32 * j + lr;
-    const float sm = BLOCK ? fcur[j] : sx[min(m0 + wm * DTM + ml, M - 1)];
+    const float sm = BLOCK ? fcur[j] : scl[wm * DTM + ml];
 #pragma unroll
     for (int i = 0; i < DNI; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int nl = 32 * i + 8 * q + 4 * kh;
-        const int n = n0 + wn * DTN + nl;
         uint2 pk;
         if constexpr (BLOCK) {  // sum counted in units of the last factor
           pk.x = pack_bf16x2(acc[i][j][4 * q + 0] * sm, acc[i][j][4 * q + 1] * sm);
           pk.y = pack_bf16x2(acc[i][j][4 * q + 2] * sm, acc[i][j][4 * q + 3] * sm);
         } else {
-          float s4[4];
-          if (n + 3 < N) {
-            const float4 t = *reinterpret_cast<const float4*>(sw + n);
-            s4[0] = t.x; s4[1] = t.y; s4[2] = t.z; s4[3] = t.w;
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s4[r] = (n + r < N) ? sw[n + r] : 0.f;
-          }
-          pk.x = pack_bf16x2(acc[i][j][4 * q + 0] * sm * s4[0], acc[i][j][4 * q + 1] * sm * s4[1]);
-          pk.y = pack_bf16x2(acc[i][j][4 * q + 2] * sm * s4[2], acc[i][j][4 * q + 3] * sm * s4[3]);
+          const float4 s4 = *reinterpret_cast<const float4*>(scl + BM + wn * DTN + nl);
+          pk.x = pack_bf16x2(acc[i][j][4 * q + 0] * sm * s4.x, acc[i][j][4 * q + 1] * sm * s4.y);
+          pk.y = pack_bf16x2(acc[i][j][4 * q + 2] * sm * s4.z, acc[i][j][4 * q + 3] * sm * s4.w);
         }
         *reinterpret_cast<uint2*>(ep + ml * EPI + nl * 2) = pk;
       }
