@@ -49,6 +49,8 @@ int check_gemm_args(const uint8_t* qx, const float* sx, const uint8_t* qw,
   if (block && (N % 128) != 0) return FP8DQ_ERR_SHAPE;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return FP8DQ_ERR_SHAPE;
   if (!known_flags(flags)) return FP8DQ_ERR_FLAGS;
+  // prefill: the weight operand is addressed with 32-bit byte offsets
+  if (!use_decode(M, flags) && N * K >= (int64_t(1) << 32)) return FP8DQ_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8DQ_OK;
   if (!qx || !sx || !qw || !sw || !y) return FP8DQ_ERR_NULL;
   if (!aligned16(qx) || !aligned16(sx) || !aligned16(qw) || !aligned16(sw) ||
@@ -68,8 +70,20 @@ int run_gemm(const uint8_t* qx, const float* sx, const uint8_t* qw,
              const float* sw, void* y, int64_t M, int64_t N, int64_t K,
              uint32_t flags, void* ws, bool block, hipStream_t st) {
   if (!use_decode(M, flags)) {
-    fp8dq::launch_gemm_prefill(qx, sx, qw, sw, y, M, N, K, block, st);
-    return launch_status();
+    // The prefill kernels address an operand with 32-bit byte offsets: run
+    // row blocks of X small enough for that (W itself must stay below 4 GiB,
+    // checked with the arguments).
+    const int64_t G = K / 128;
+    int64_t rows_max = ((int64_t(1) << 32) - 1) / K;
+    rows_max -= rows_max % 256;
+    for (int64_t m0 = 0; m0 < M; m0 += rows_max) {
+      const int64_t rows = (M - m0) < rows_max ? (M - m0) : rows_max;
+      fp8dq::launch_gemm_prefill(qx + m0 * K, sx + (block ? m0 * G : m0), qw, sw,
+                                 static_cast<uint16_t*>(y) + m0 * N, rows, N, K, block, st);
+      const int s = launch_status();
+      if (s != FP8DQ_OK) return s;
+    }
+    return FP8DQ_OK;
   }
   const int64_t G = K / 128;
   for (int64_t m0 = 0; m0 < M; m0 += FP8DQ_DECODE_MAX_M) {
