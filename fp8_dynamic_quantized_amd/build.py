@@ -39,9 +39,17 @@ def _sources():
     return [os.path.join(CSRC, f) for f in srcs]
 
 
+# Per-source flags. gemm_block.hip: keep MFMA accumulators in ordinary VGPRs
+# (the block kernel rescales its accumulator every 128 K columns).
+PER_SOURCE = {
+    "gemm_block.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str, build_dir: str = BUILD, defines=()) -> str:
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
+    extra = PER_SOURCE.get(os.path.basename(src), [])
+    cmd = [HIPCC, *COMMON, *extra, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -113,4 +113,16 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
       : "memory", "m0");
 }
 
+// One global_load_lds_dword: 4 bytes from base + off (off per lane) to LDS
+// byte address lds + 4 * lane (M0 = lds). Completion is observed with vmcnt.
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, %1"
+      :
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory", "m0");
+}
+
 }  // namespace fp8dq

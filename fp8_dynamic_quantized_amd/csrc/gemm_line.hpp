@@ -1,0 +1,353 @@
+// Whole-line prefill GEMM kernels (gfx950), shared by the per-channel
+// instantiation (gemm_prefill.hip) and the block instantiation
+// (gemm_block.hip, built with the MFMA accumulators in ordinary VGPRs so the
+// per-group rescale is a plain multiply).
+//
+// What is computed: Y[m,n] = bf16( sum_k val(qx[m,k]) val(qw[n,k]) * scales ),
+// per-token x per-channel scales (Llama-3.1-8B-Instruct-FP8-Dynamic page, FP8
+// dynamic quantization table) or 128-wide activation groups x 128 x 128
+// weight blocks (Llama-3.2-3B-Instruct-FP8-Block page, FP8 block
+// quantization table).
+#pragma once
+#include "device_common.hpp"
+
+#include <mutex>
+#include <type_traits>
+
+namespace fp8dq {
+namespace line {
+namespace {
+
+constexpr int GM = 8;  // tile rows per L2 group
+// s_waitcnt immediate (gfx9 encoding): at most n vector-memory operations of
+// this wave outstanding (expcnt / lgkmcnt not waited on).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+// ---------------------------------------------------------------------------
+// Whole-line kernels: 256 x BN tiles (BN = 256 per-channel, 128 block),
+// v_mfma_f32_32x32x64_f8f6f4, 4 waves (2 x 2).
+//  * A load instruction moves 8 rows x 128 bytes (two 64-byte MFMA K steps of
+//    each row): every request is a whole 128-byte line. The L2 -> LDS path
+//    costs the same per line touched, so 64-byte row pieces (16 rows per
+//    instruction) reached only half the bytes per cycle.
+//  * LDS: NSL pair slots [X: 256 rows | W: BN rows], rows of 128 bytes whose
+//    16-byte chunks are XOR-permuted by row bits 0-4 (conflict-free fragment
+//    reads; fragments 32 rows apart sit at a constant distance); then the
+//    scale areas, filled by 4-byte-per-lane direct loads.
+//  * Step kt runs the MFMAs of K step kt while reading the fragments of step
+//    kt+1 from LDS. Pairs are issued on odd steps: at step 2P+1 pair P+NSL
+//    goes into the slot of pair P. Every wave has waited (lgkmcnt) for its
+//    reads of that slot -- issued during step 2P, at the front of the step --
+//    before the barrier of step 2P+1, so the refill never races a read. Odd
+//    steps wait for the pair read next and hold the only barrier; even steps
+//    read the second half of a pair that has already landed.
+//  * Per-channel: NSL = 2 (two 64 KB slots), the tile's sx / sw in LDS.
+//  * Block (128 x 128 weight blocks, 128-wide activation groups): NSL = 3
+//    (48 KB slots); a pair is exactly one scale group g, whose 256 activation
+//    scales ride with the pair into a per-slot LDS ring, and the tile's
+//    weight-block scales for every g are loaded once. One accumulator carries
+//    the sum in units of the current factor f_g = sx[m,g] * sw[nb,g]: it is
+//    multiplied by f_{g-1} / f_g before group g's first MFMAs (a zero factor,
+//    an all-zero group, leaves it alone) and by the last factor at the end.
+//  * Epilogue from registers: scale, round to bf16, and pair lanes l and l+32
+//    with v_permlane32_swap so each lane stores 16 contiguous bytes.
+// ---------------------------------------------------------------------------
+constexpr int LBK = 128;                 // K bytes per pair (two MFMA steps)
+
+template <bool BLOCK>
+struct LineCfg {
+  static constexpr int BM = 256, BN = BLOCK ? 128 : 256;
+  static constexpr int NSL = BLOCK ? 3 : 2;                 // pair slots
+  static constexpr int SLOT = (BM + BN) * LBK;
+  static constexpr int XQ = BM / 32, WQ = BN / 32;          // loads per wave per pair
+  static constexpr int NLD = XQ + WQ;
+  static constexpr int SC = NSL * SLOT;                     // scale areas
+  // per-channel: sx [256] + sw [256]; block: sx ring NSL x [256], then sw [G]
+  static constexpr int SWB = SC + (BLOCK ? NSL * 1024 : 2048);
+  static size_t smem(int64_t K) {   // block: sw loaded in 64-entry chunks
+    return (size_t)SWB + (BLOCK ? (size_t)((K / 128 + 63) / 64) * 256 : 0);
+  }
+};
+
+__device__ __forceinline__ int lswz(int row) { return (row & 7) ^ ((row >> 3) & 3); }
+
+__device__ __forceinline__ uint32_t pk_bf16_rne(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+template <bool BLOCK>
+__global__ __launch_bounds__(256, 1) void gemm_prefill_line_kernel(
+    const uint8_t* __restrict__ qx, const float* __restrict__ sx,
+    const uint8_t* __restrict__ qw, const float* __restrict__ sw,
+    uint16_t* __restrict__ y, int M, int N, int K, int tiles_m, int tiles_n) {
+  using C = LineCfg<BLOCK>;
+  constexpr int BM = C::BM, BN = C::BN, NSL = C::NSL, SLOT = C::SLOT;
+  constexpr int XQ = C::XQ, WQ = C::WQ, NLD = C::NLD;
+  constexpr int DTM = 128, DTN = BN / 2;
+  constexpr int DMJ = DTM / 32, DNI = DTN / 32;   // 32-row fragments per wave (m, n)
+  constexpr int NM = DNI * DMJ;                   // MFMAs per step
+  constexpr int NR = 2 * (DNI + DMJ);             // fragment halves per step
+  constexpr int RPE = (NR + NM - 1) / NM;         // reads per MFMA slot, odd steps
+  constexpr int NSC = BLOCK ? 1 : 0;              // scale loads per pair
+  constexpr int XB = BM * LBK;                    // W part of a slot
+  static_assert(2 * NM >= NR, "even steps read two halves per MFMA");
+  constexpr int IPS = (NLD + NSC + NM - 1) / NM;  // loads issued per MFMA slot, odd steps
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  const int nblk = gridDim.x;
+  int bid = blockIdx.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int group = GM * tiles_n;
+  const int first_m = (bid / group) * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int in_g = bid % group;
+  const int m0 = (first_m + in_g % gm) * BM;
+  const int n0 = (in_g / gm) * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int lr = lane & 31, kh = lane >> 5;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)smem;
+  const int G = K / 128;                          // pairs = scale groups
+
+  // Loads: groups of 8 rows; wave w takes groups 4q + w. Lane l covers row
+  // 8g + l/8 and LDS chunk slot l%8, i.e. global chunk (l%8) ^ lswz(row)
+  // = (l%8) ^ (l/8) ^ w (independent of q).
+  const int rl = lane >> 3;
+  const uint32_t c16 = (uint32_t)(((lane & 7) ^ rl ^ wave) << 4);
+  uint32_t rowX[XQ], rowW[WQ];
+#pragma unroll
+  for (int q = 0; q < XQ; ++q)
+    rowX[q] = (uint32_t)min(m0 + 32 * q + 8 * wave + rl, M - 1) * (uint32_t)K + c16;
+#pragma unroll
+  for (int q = 0; q < WQ; ++q)
+    rowW[q] = (uint32_t)min(n0 + 32 * q + 8 * wave + rl, N - 1) * (uint32_t)K + c16;
+  // block: this wave's 64 rows of activation scales, group g -> ring slot
+  const uint32_t sxoff = BLOCK ? (uint32_t)min(m0 + 64 * wave + lane, M - 1) * (uint32_t)G * 4u : 0u;
+  // load u of pair p (clamped to the last one) into slot index si
+  auto issue = [&](int si, int p, int u) {
+    const int pc = min(p, G - 1);
+    if (u < NLD) {
+      const size_t koff = (size_t)pc * LBK;
+      const uint32_t sb = lds0 + (uint32_t)(si * SLOT);
+      if (u < XQ) dma16(qx + koff, rowX[u], sb + (uint32_t)((4 * u + wave) * 1024));
+      else dma16(qw + koff, rowW[u - XQ], sb + XB + (uint32_t)((4 * (u - XQ) + wave) * 1024));
+    } else if (BLOCK && u == NLD) {
+      dma4(sx, sxoff + (uint32_t)pc * 4u, lds0 + C::SC + (uint32_t)(si * 1024 + 256 * wave));
+    }
+  };
+  if constexpr (BLOCK) {
+    // the tile's weight-block scales for every group (its 128 columns are one block)
+    const uint32_t swrow = (uint32_t)(n0 / 128) * (uint32_t)G * 4u;
+    for (int c = wave; c * 64 < G; c += 4)
+      dma4(sw, swrow + (uint32_t)min(64 * c + lane, G - 1) * 4u,
+           lds0 + C::SWB + (uint32_t)(256 * c));
+  } else {
+    // the tile's scales: 64 sx (rows) and 64 sw (columns) per wave
+    dma4(sx, (uint32_t)min(m0 + 64 * wave + lane, M - 1) * 4u, lds0 + C::SC + 256 * wave);
+    dma4(sw, (uint32_t)min(n0 + 64 * wave + lane, N - 1) * 4u, lds0 + C::SC + 1024 + 256 * wave);
+  }
+
+  // fragment offsets: row r = base + 32 f, chunk c = 4 par + 2 kh + h
+  const int arow0 = wn * DTN + lr, brow0 = wm * DTM + lr;
+  const int sz = lswz(lr);
+  uint32_t oA[2][2], oB[2][2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = (4 * par + 2 * kh + h) ^ sz;
+      oA[par][h] = (uint32_t)(XB + arow0 * LBK + (c << 4));
+      oB[par][h] = (uint32_t)(brow0 * LBK + (c << 4));
+    }
+  auto rd_at = [&](v8i& f, const uint8_t* p, int h) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    f[4 * h + 0] = v.x; f[4 * h + 1] = v.y; f[4 * h + 2] = v.z; f[4 * h + 3] = v.w;
+  };
+  // read order A0, B0 .. B(DMJ-1), A1 .. : the order of first use
+  auto frag_of = [](int o) { return o == 0 ? 0 : (o <= DMJ ? DNI + o - 1 : o - DMJ); };
+  auto read_frag = [&](v8i (&Af)[DNI], v8i (&Bf)[DMJ], int si, int par, int f, int h) {
+    const uint8_t* base = smem + si * SLOT;
+    if (f < DNI) rd_at(Af[f], base + oA[par][h] + 4096 * f, h);
+    else rd_at(Bf[f - DNI], base + oB[par][h] + 4096 * (f - DNI), h);
+  };
+
+  v16f acc[DNI][DMJ];
+#pragma unroll
+  for (int i = 0; i < DNI; ++i)
+#pragma unroll
+    for (int j = 0; j < DMJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  // block: factor the accumulator is counted in, per row j, and the rescale
+  // for the next group (formed one step ahead)
+  float fcur[DMJ], fnext[DMJ], rho[DMJ];
+#pragma unroll
+  for (int j = 0; j < DMJ; ++j) { fcur[j] = 0.f; fnext[j] = 0.f; rho[j] = 1.f; }
+  auto group_factor = [&](int g, int si) {   // f_g of this lane's rows -> rho, fcur
+    const float* sxs = reinterpret_cast<const float*>(smem + C::SC + si * 1024);
+    const float swg = reinterpret_cast<const float*>(smem + C::SWB)[min(g, G - 1)];
+#pragma unroll
+    for (int j = 0; j < DMJ; ++j) {
+      const float f = sxs[wm * DTM + 32 * j + lr] * swg;
+      const bool live = f != 0.0f;
+      rho[j] = live ? fcur[j] * __builtin_amdgcn_rcpf(f) : 1.0f;
+      fnext[j] = live ? f : fcur[j];
+    }
+  };
+
+  // prologue: pairs 0 .. NSL-1 in flight, wait for pair 0 (and the scales)
+#pragma unroll
+  for (int pp = 0; pp < NSL; ++pp)
+#pragma unroll
+    for (int u = 0; u < NLD + NSC; ++u) issue(pp, pp, u);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NSL - 1) * (NLD + NSC)));
+  __syncthreads();
+  v8i A[2][DNI], B[2][DMJ];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) read_frag(A[0], B[0], 0, 0, frag_of(r >> 1), r & 1);
+  if constexpr (BLOCK) {
+    group_factor(0, 0);
+#pragma unroll
+    for (int j = 0; j < DMJ; ++j) fcur[j] = fnext[j];   // rho of group 0 is unused
+  }
+
+  int cs = 0;  // slot index of the pair the current step belongs to
+  // Step kt (cur = kt & 1). Even: read step kt+1 (same pair, second half),
+  // two reads per MFMA at the front of the step; block: rescale each
+  // accumulator block before its first MFMA of the group. Odd: wait for the
+  // next pair, barrier, read step kt+1 from the next slot, refill this
+  // pair's slot with pair kt/2 + NSL; block: form the next group's rescale.
+  auto step = [&](int kt, auto cur_c, auto more_c) {
+    constexpr int cur = decltype(cur_c)::value;
+    constexpr bool more = decltype(more_c)::value;
+    const int ns = cs + 1 == NSL ? 0 : cs + 1;
+    if (cur == 1 && more) {
+      // vmcnt: the NSL-2 newer pairs may stay in flight; lgkmcnt(0): this
+      // wave's reads of the slot refilled below are done
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NSL - 2) * (NLD + NSC)) & ~0x0F00);
+      asm volatile("s_barrier" ::: "memory");
+      if constexpr (BLOCK) group_factor(kt / 2 + 1, ns);
+    }
+    const int rs = cur == 0 ? cs : ns;
+#pragma unroll
+    for (int t = 0; t < NM; ++t) {
+      if (more) {
+        if (cur == 0) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r = 2 * t + u;
+            if (r < NR) read_frag(A[1], B[1], rs, 1, frag_of(r >> 1), r & 1);
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < RPE; ++u) {
+            const int r = RPE * t + u;
+            if (r < NR) read_frag(A[0], B[0], rs, 0, frag_of(r >> 1), r & 1);
+          }
+#pragma unroll
+          for (int u = 0; u < IPS; ++u) {
+            const int v = IPS * t + u;
+            if (v < NLD + NSC) issue(cs, kt / 2 + NSL, v);
+          }
+        }
+      }
+      const int i = t / DMJ, j = t % DMJ;
+      if constexpr (BLOCK && cur == 0) {   // rho = 1 before group 1
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] *= rho[j];
+      }
+      acc[i][j] = mfma_e4m3_32x32x64(A[cur][i], B[cur][j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (BLOCK && cur == 1) {
+#pragma unroll
+      for (int j = 0; j < DMJ; ++j) fcur[j] = fnext[j];
+    }
+    if (cur == 1) cs = ns;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  const int KT = K / 64;   // even, >= 4
+  step(0, I0(), std::true_type());
+  step(1, I1(), std::true_type());
+  for (int kt = 2; kt < KT - 2; kt += 2) {
+    step(kt, I0(), std::true_type());
+    step(kt + 1, I1(), std::true_type());
+  }
+  step(KT - 2, I0(), std::true_type());
+  step(KT - 1, I1(), std::false_type());
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // no load may still target LDS
+
+  // ---- epilogue ----
+  const float* scl = reinterpret_cast<const float*>(smem + C::SC);
+  float smv[DMJ];
+#pragma unroll
+  for (int j = 0; j < DMJ; ++j) smv[j] = BLOCK ? fcur[j] : scl[wm * DTM + 32 * j + lr];
+  const bool vec = (N & 7) == 0;
+#pragma unroll
+  for (int i = 0; i < DNI; ++i) {
+    float4 s4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      s4[q] = BLOCK ? make_float4(1.f, 1.f, 1.f, 1.f)
+                    : *reinterpret_cast<const float4*>(scl + 256 + wn * DTN + 32 * i + 8 * q + 4 * kh);
+#pragma unroll
+    for (int j = 0; j < DMJ; ++j) {
+      const int m = m0 + wm * DTM + 32 * j + lr;
+      const float sm = smv[j];
+#pragma unroll
+      for (int qp = 0; qp < 2; ++qp) {
+        uint32_t w[2][2];   // [q of the pair][dword]
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int q = 2 * qp + u;
+          w[u][0] = pk_bf16_rne(acc[i][j][4 * q + 0] * sm * s4[q].x, acc[i][j][4 * q + 1] * sm * s4[q].y);
+          w[u][1] = pk_bf16_rne(acc[i][j][4 * q + 2] * sm * s4[q].z, acc[i][j][4 * q + 3] * sm * s4[q].w);
+        }
+        // lane l (kh 0) keeps its q = 2qp values and takes lane l+32's; lane
+        // l+32 keeps its q = 2qp+1 values and takes lane l's
+        const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
+        const uint4 v = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+        const int n = n0 + wn * DTN + 32 * i + 16 * qp + 8 * kh;
+        if (m < M) {
+          uint16_t* out = y + (int64_t)m * N + n;
+          if (vec && n + 7 < N) {
+            *reinterpret_cast<uint4*>(out) = v;
+          } else {
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (n + e < N) out[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
+    }
+  }
+}
+
+template <bool BLOCK>
+void launch_line(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
+                 void* y, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  using C = LineCfg<BLOCK>;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_prefill_line_kernel<BLOCK>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  });
+  const int tiles_m = (int)((M + C::BM - 1) / C::BM);
+  const int tiles_n = (int)((N + C::BN - 1) / C::BN);
+  hipLaunchKernelGGL((gemm_prefill_line_kernel<BLOCK>), dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(256), C::smem(K), st, qx, sx, qw, sw, (uint16_t*)y, (int)M, (int)N,
+                     (int)K, tiles_m, tiles_n);
+}
+
+}  // namespace
+}  // namespace line
+}  // namespace fp8dq

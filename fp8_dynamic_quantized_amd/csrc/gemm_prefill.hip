@@ -26,6 +26,7 @@
 //    same XCD (ids are dealt round-robin over the 8 XCDs) and, within an
 //    XCD, in groups of GM tile rows for L2 reuse.
 #include "device_common.hpp"
+#include "gemm_line.hpp"
 #include "kernels.hpp"
 
 #include <mutex>
@@ -273,17 +274,6 @@ __device__ __forceinline__ int dlds_off(int row, int c) {
   return (row >> 4) * 1024 + ((dq(row & 15) << 2) + (c ^ dh(row))) * 16;
 }
 
-// One global_load_lds_dword: 4 bytes from base + off (off per lane) to LDS
-// byte address lds + 4 * lane (M0 = lds). Completion is observed with vmcnt.
-__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %0, %1"
-      :
-      : "v"(off), "s"(base), "s"(lds)
-      : "memory", "m0");
-}
 
 // BN: tile width (256 or 128); S: ring slots; WPC: workgroups per CU the
 // register / LDS budget is sized for (two let one workgroup's MFMAs cover the
@@ -596,242 +586,6 @@ __global__ __launch_bounds__(256, WPC) void gemm_prefill_deep_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------
-// Whole-line per-channel kernel: 256 x 256 tiles, v_mfma_f32_32x32x64_f8f6f4.
-//  * A load instruction moves 8 rows x 128 bytes (two 64-byte MFMA K steps of
-//    each row): every request is a whole 128-byte line. The L2 -> LDS path
-//    costs the same per line touched, so 64-byte row pieces (16 rows per
-//    instruction) reached only half the bytes per cycle.
-//  * LDS: two 64 KB pair slots [X: 256 rows | W: 256 rows], rows of 128 bytes
-//    whose 16-byte chunks are XOR-permuted by row bits 0-4 (conflict-free
-//    fragment reads; fragments 32 rows apart sit at a constant distance);
-//    then two 2 KB scale buffers (sx of the tile's rows, sw of its columns),
-//    filled by 4-byte-per-lane direct loads.
-//  * Step kt runs the MFMAs of K step kt while reading the fragments of step
-//    kt+1 from LDS. Pairs are issued on odd steps: at step 2P+1 pair P+2 goes
-//    into the slot of pair P. Every wave has waited (lgkmcnt) for its reads of
-//    that slot -- issued during step 2P, at the front of the step -- before the
-//    barrier of step 2P+1, so the refill never races a read. Odd steps wait
-//    for every load (the pair read next) and hold the only barrier; even
-//    steps read the second half of a pair that has already landed.
-//  * Epilogue from registers: scale, round to bf16, and pair lanes l and l+32
-//    with v_permlane32_swap so each lane stores 16 contiguous bytes.
-// ---------------------------------------------------------------------------
-constexpr int LBK = 128;                 // K bytes per pair (two MFMA steps)
-constexpr int LSLOT = 512 * LBK;         // pair slot: X 256 rows + W 256 rows
-constexpr int LXB = 256 * LBK;           // W part of a slot
-constexpr int LSCL = 2 * LSLOT;          // scale buffers: 2 x (256 sx + 256 sw) floats
-constexpr int LSMEM = LSCL + 2 * 2048;
-
-__device__ __forceinline__ int lswz(int row) { return (row & 7) ^ ((row >> 3) & 3); }
-
-__device__ __forceinline__ uint32_t pk_bf16_rne(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
-__global__ __launch_bounds__(256, 1) void gemm_prefill_line_kernel(
-    const uint8_t* __restrict__ qx, const float* __restrict__ sx,
-    const uint8_t* __restrict__ qw, const float* __restrict__ sw,
-    uint16_t* __restrict__ y, int M, int N, int K, int tiles_m, int tiles_n) {
-  constexpr int BM = 256, BN = 256, DTM = 128, DTN = 128;
-  constexpr int DMJ = 4, DNI = 4;                 // 32-row fragments per wave (m, n)
-  constexpr int NM = DNI * DMJ;                   // MFMAs per step
-  constexpr int NR = 2 * (DNI + DMJ);             // fragment halves per step
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-
-  const int nblk = gridDim.x;
-  int bid = blockIdx.x;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int group = GM * tiles_n;
-  const int first_m = (bid / group) * GM;
-  const int gm = min(tiles_m - first_m, GM);
-  const int in_g = bid % group;
-  const int m0 = (first_m + in_g % gm) * BM;
-  const int n0 = (in_g / gm) * BN;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
-  const int lr = lane & 31, kh = lane >> 5;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)smem;
-
-  // loads: 32 groups of 8 rows per operand; wave w takes groups 4q + w. Lane l
-  // covers row 8g + l/8 and LDS chunk slot l%8, i.e. global chunk
-  // (l%8) ^ lswz(row) = (l%8) ^ (l/8) ^ w (independent of q).
-  const int rl = lane >> 3;
-  const uint32_t c16 = (uint32_t)(((lane & 7) ^ rl ^ wave) << 4);
-  uint32_t rowX[8], rowW[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int r = 32 * q + 8 * wave + rl;
-    rowX[q] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + c16;
-    rowW[q] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + c16;
-  }
-  const int KP = K / LBK;
-  // pair p (clamped to the last one) into slot byte offset `slot`; load
-  // number u = 0..15 of the wave (X groups, then W groups)
-  auto issue_pair_load = [&](uint32_t slot, int p, int u) {
-    const size_t koff = (size_t)min(p, KP - 1) * LBK;
-    const int q = u & 7;
-    if (u < 8) dma16(qx + koff, rowX[q], lds0 + slot + (uint32_t)((4 * q + wave) * 1024));
-    else dma16(qw + koff, rowW[q], lds0 + slot + LXB + (uint32_t)((4 * q + wave) * 1024));
-  };
-  // the tile's scales: 64 sx (rows) and 64 sw (columns) per wave
-  dma4(sx, (uint32_t)min(m0 + 64 * wave + lane, M - 1) * 4u, lds0 + LSCL + 256 * wave);
-  dma4(sw, (uint32_t)min(n0 + 64 * wave + lane, N - 1) * 4u, lds0 + LSCL + 1024 + 256 * wave);
-
-  // fragment offsets: row r = base + 32 f, chunk c = 4 par + 2 kh + h
-  const int arow0 = wn * DTN + lr, brow0 = wm * DTM + lr;
-  const int sz = lswz(lr);
-  uint32_t oA[2][2], oB[2][2];
-#pragma unroll
-  for (int par = 0; par < 2; ++par)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = (4 * par + 2 * kh + h) ^ sz;
-      oA[par][h] = (uint32_t)(LXB + arow0 * LBK + (c << 4));
-      oB[par][h] = (uint32_t)(brow0 * LBK + (c << 4));
-    }
-  auto rd_at = [&](v8i& f, const uint8_t* p, int h) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    f[4 * h + 0] = v.x; f[4 * h + 1] = v.y; f[4 * h + 2] = v.z; f[4 * h + 3] = v.w;
-  };
-  auto frag_of = [](int o) { return o == 0 ? 0 : (o <= DMJ ? DNI + o - 1 : o - DMJ); };
-  auto read_frag = [&](v8i (&Af)[DNI], v8i (&Bf)[DMJ], uint32_t slot, int par, int f, int h) {
-    if (f < DNI) rd_at(Af[f], smem + slot + oA[par][h] + 4096 * f, h);
-    else rd_at(Bf[f - DNI], smem + slot + oB[par][h] + 4096 * (f - DNI), h);
-  };
-
-  v16f acc[DNI][DMJ];
-#pragma unroll
-  for (int i = 0; i < DNI; ++i)
-#pragma unroll
-    for (int j = 0; j < DMJ; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  // prologue: pairs 0 and 1 in flight, wait for pair 0 (and the scales)
-#pragma unroll
-  for (int u = 0; u < 16; ++u) issue_pair_load(0u, 0, u);
-#pragma unroll
-  for (int u = 0; u < 16; ++u) issue_pair_load((uint32_t)LSLOT, 1, u);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
-  __syncthreads();
-  v8i A[2][DNI], B[2][DMJ];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) read_frag(A[0], B[0], 0u, 0, frag_of(r >> 1), r & 1);
-
-  uint32_t cslot = 0;  // slot of the pair the current step belongs to
-  // Step kt (cur = kt & 1). Even: read step kt+1 (same pair, second half),
-  // two reads per MFMA at the front of the step. Odd: wait for the next pair,
-  // barrier, read step kt+1 from the other slot one read per MFMA, and refill
-  // this pair's slot with pair kt/2 + 2.
-  auto step = [&](int kt, auto cur_c, auto more_c) {
-    constexpr int cur = decltype(cur_c)::value;
-    constexpr bool more = decltype(more_c)::value;
-    if (cur == 1 && more) {
-      __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) expcnt(0) lgkmcnt(0)
-      asm volatile("s_barrier" ::: "memory");
-    }
-    const uint32_t rslot = cur == 0 ? cslot : (cslot ^ (uint32_t)LSLOT);
-#pragma unroll
-    for (int t = 0; t < NM; ++t) {
-      if (more) {
-        if (cur == 0) {
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int r = 2 * t + u;
-            if (r < NR) read_frag(A[1], B[1], rslot, 1, frag_of(r >> 1), r & 1);
-          }
-        } else {
-          if (t < NR) read_frag(A[0], B[0], rslot, 0, frag_of(t >> 1), t & 1);
-          issue_pair_load(cslot, kt / 2 + 2, t);
-        }
-      }
-      const int i = t / DMJ, j = t % DMJ;
-      acc[i][j] = mfma_e4m3_32x32x64(A[cur][i], B[cur][j], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (cur == 1) cslot ^= (uint32_t)LSLOT;
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  const int KT = K / 64;   // even, >= 4
-  step(0, I0(), std::true_type());
-  step(1, I1(), std::true_type());
-  for (int kt = 2; kt < KT - 2; kt += 2) {
-    step(kt, I0(), std::true_type());
-    step(kt + 1, I1(), std::true_type());
-  }
-  step(KT - 2, I0(), std::true_type());
-  step(KT - 1, I1(), std::false_type());
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // no load may still target LDS
-
-  // ---- epilogue ----
-  const float* scl = reinterpret_cast<const float*>(smem + LSCL);
-  float smv[DMJ];
-#pragma unroll
-  for (int j = 0; j < DMJ; ++j) smv[j] = scl[wm * DTM + 32 * j + lr];
-  const bool vec = (N & 7) == 0;
-#pragma unroll
-  for (int i = 0; i < DNI; ++i) {
-    float4 s4[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      s4[q] = *reinterpret_cast<const float4*>(scl + 256 + wn * DTN + 32 * i + 8 * q + 4 * kh);
-#pragma unroll
-    for (int j = 0; j < DMJ; ++j) {
-      const int m = m0 + wm * DTM + 32 * j + lr;
-      const float sm = smv[j];
-#pragma unroll
-      for (int qp = 0; qp < 2; ++qp) {
-        uint32_t w[2][2];   // [q of the pair][dword]
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int q = 2 * qp + u;
-          w[u][0] = pk_bf16_rne(acc[i][j][4 * q + 0] * sm * s4[q].x, acc[i][j][4 * q + 1] * sm * s4[q].y);
-          w[u][1] = pk_bf16_rne(acc[i][j][4 * q + 2] * sm * s4[q].z, acc[i][j][4 * q + 3] * sm * s4[q].w);
-        }
-        // lane l (kh 0) keeps its q = 2qp values and takes lane l+32's; lane
-        // l+32 keeps its q = 2qp+1 values and takes lane l's
-        const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
-        const auto s1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
-        const uint4 v = make_uint4(s0[0], s1[0], s0[1], s1[1]);
-        const int n = n0 + wn * DTN + 32 * i + 16 * qp + 8 * kh;
-        if (m < M) {
-          uint16_t* out = y + (int64_t)m * N + n;
-          if (vec && n + 7 < N) {
-            *reinterpret_cast<uint4*>(out) = v;
-          } else {
-            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (n + e < N) out[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
-          }
-        }
-      }
-    }
-  }
-}
-
-void launch_line(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
-                 void* y, int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  static std::once_flag once;
-  std::call_once(once, [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_prefill_line_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, LSMEM);
-  });
-  const int tiles_m = (int)((M + 255) / 256);
-  const int tiles_n = (int)((N + 255) / 256);
-  hipLaunchKernelGGL(gemm_prefill_line_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(256),
-                     LSMEM, st, qx, sx, qw, sw, (uint16_t*)y, (int)M, (int)N, (int)K, tiles_m,
-                     tiles_n);
-}
-
 template <int BN, int S, int WPC, bool BLOCK = false>
 void launch_deep(const uint8_t* qx, const float* sx, const uint8_t* qw,
                  const float* sw, void* y, int64_t M, int64_t N, int64_t K,
@@ -899,7 +653,9 @@ void launch_gemm_prefill(const uint8_t* qx, const float* sx, const uint8_t* qw,
 #else
     const bool deep = deep_ok;
 #endif
-    if (deep) {
+    if (deep && K >= 256) {
+      launch_gemm_line_block(qx, sx, qw, sw, y, M, N, K, st);
+    } else if (deep) {
       launch_deep<128, 5, 1, true>(qx, sx, qw, sw, y, M, N, K, st);
     }
     else if (use_big) launch_cfg<256, 256, true>(qx, sx, qw, sw, y, M, N, K, st);
@@ -912,7 +668,7 @@ void launch_gemm_prefill(const uint8_t* qx, const float* sx, const uint8_t* qw,
 #elif defined(FP8DQ_TILE_OVERRIDE) && FP8DQ_TILE_OVERRIDE == 5
     launch_deep<256, 4, 1>(qx, sx, qw, sw, y, M, N, K, st);
 #else
-    if (use_big && K >= 256) launch_line(qx, sx, qw, sw, y, M, N, K, st);
+    if (use_big && K >= 256) line::launch_line<false>(qx, sx, qw, sw, y, M, N, K, st);
     else if (use_big) launch_deep<256, 5, 1>(qx, sx, qw, sw, y, M, N, K, st);
     else launch_cfg<256, 128, false>(qx, sx, qw, sw, y, M, N, K, st);
 #endif

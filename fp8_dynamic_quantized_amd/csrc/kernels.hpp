@@ -19,6 +19,11 @@ void launch_quant_wblock(const void* w, int64_t N, int64_t K, uint8_t* q,
 // Prefill GEMM (gemm_prefill.hip): LDS-tiled MFMA, fused epilogue.
 // block = false: per-channel scales sx[M], sw[N];
 // block = true : sx[M, K/128], sw[N/128, K/128].
+// Whole-line block-scaled prefill GEMM (gemm_block.hip); K >= 256,
+// K <= 131072, 32-bit operand and scale offsets.
+void launch_gemm_line_block(const uint8_t* qx, const float* sx, const uint8_t* qw,
+                            const float* sw, void* y, int64_t M, int64_t N, int64_t K,
+                            hipStream_t st);
 void launch_gemm_prefill(const uint8_t* qx, const float* sx, const uint8_t* qw,
                          const float* sw, void* y, int64_t M, int64_t N,
                          int64_t K, bool block, hipStream_t st);
