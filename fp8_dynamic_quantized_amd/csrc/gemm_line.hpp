@@ -290,17 +290,20 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_line_kernel(
 #pragma unroll
   for (int j = 0; j < DMJ; ++j) smv[j] = BLOCK ? fcur[j] : scl[wm * DTM + 32 * j + lr];
   const bool vec = (N & 7) == 0;
+  // j outer, then i and qp: a lane's eight stores of one row (the wave's
+  // 2 * DTN bytes of it) go out back to back, so each 128-byte line of Y is
+  // completed by consecutive stores rather than written back in pieces
 #pragma unroll
-  for (int i = 0; i < DNI; ++i) {
-    float4 s4[4];
+  for (int j = 0; j < DMJ; ++j) {
+    const int m = m0 + wm * DTM + 32 * j + lr;
+    const float sm = smv[j];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      s4[q] = BLOCK ? make_float4(1.f, 1.f, 1.f, 1.f)
-                    : *reinterpret_cast<const float4*>(scl + 256 + wn * DTN + 32 * i + 8 * q + 4 * kh);
+    for (int i = 0; i < DNI; ++i) {
+      float4 s4[4];
 #pragma unroll
-    for (int j = 0; j < DMJ; ++j) {
-      const int m = m0 + wm * DTM + 32 * j + lr;
-      const float sm = smv[j];
+      for (int q = 0; q < 4; ++q)
+        s4[q] = BLOCK ? make_float4(1.f, 1.f, 1.f, 1.f)
+                      : *reinterpret_cast<const float4*>(scl + 256 + wn * DTN + 32 * i + 8 * q + 4 * kh);
 #pragma unroll
       for (int qp = 0; qp < 2; ++qp) {
         uint32_t w[2][2];   // [q of the pair][dword]
