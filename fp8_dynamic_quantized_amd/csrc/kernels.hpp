@@ -34,6 +34,7 @@ struct DecodePlan {
   int nb;            // 16-row blocks of N per workgroup
   int splits;        // K slices across the grid (1: no partials)
   int kt_per_split;  // 128-wide K steps per slice
+  int line;          // 1: whole-line kernel (LDS ring), 0: register-loading kernel
 };
 DecodePlan plan_decode(int64_t M, int64_t N, int64_t K);
 size_t decode_workspace_bytes(int64_t M, int64_t N, const DecodePlan& p);
