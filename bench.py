@@ -50,7 +50,7 @@ METRIC = "FP8-dynamic linear TFLOP/s (prefill) + weight GB/s (decode), % of roof
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 DOM_KERNEL = "gemm_prefill_line_kernel<false>"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_prefill_deep_gate_up_m4096_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_prefill_line_gate_up_m4096_traffic.txt")
 KERNEL_SOURCES = ["fp8_dynamic_quantized_amd/csrc/gemm_line.hpp",
                   "fp8_dynamic_quantized_amd/csrc/gemm_prefill.hip",
                   "fp8_dynamic_quantized_amd/csrc/device_common.hpp"]
@@ -85,6 +85,8 @@ def read_traffic():
                     k, v = line.split(":", 1)
                     kv[k.strip()] = v.strip()
         if kv.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        if kv.get("kernel") != DOM_KERNEL:
             return None
         return float(kv["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):

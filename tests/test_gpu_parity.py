@@ -13,7 +13,7 @@ import torch
 import oracle.fp8dq_oracle as O
 import synth
 from gpu_util import (assert_codes_equal, assert_scales_equal, assert_y_close,
-                      dev, dev_bf16, ensure_built, host_bf16_f64, say)
+                      dev, dev_bf16, ensure_built, host_bf16_f64, host_bits, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -190,6 +190,51 @@ def test_gemm_random_codes_small_k(F):
                        f"random codes {M}x{N}x{K} flags={flags}")
 
 
+@pytest.mark.parametrize("M,N,K", [(4173, 3853, 384), (4097, 4104, 256), (4352, 4096, 1152)])
+def test_gemm_wide_tiles_ragged(F, M, N, K):
+    """Shapes with at least 256 tiles of 256 x 256 (the whole-line kernel)
+    and ragged edges: M and N off the tile grid, N % 8 != 0 (element
+    stores), K = 256 (the shortest K loop), an odd number of 128-column
+    groups. Every output is compared."""
+    say(f"gemm wide {M}x{N}x{K}")
+    rng = np.random.default_rng(M + N + K)
+    qx = rng.choice(FINITE, size=(M, K))
+    qw = rng.choice(FINITE, size=(N, K))
+    sx = rng.uniform(1e-4, 1e-3, M).astype(np.float32)
+    sw = rng.uniform(1e-4, 1e-3, N).astype(np.float32)
+    y = F.fp8_gemm(dev(qx), dev(sx), dev(qw), dev(sw), flags=1)
+    torch.cuda.synchronize()
+    assert_y_close(host_bf16_f64(y), O.linear_per_channel(qx, sx, qw, sw), "y")
+
+
+def test_linear_x_beyond_4gib(F):
+    """fp8_linear with M * K > 2^32 bytes of X codes: the prefill path runs
+    row blocks so that each block's operand offsets fit 32 bits; rows on
+    both sides of the block boundary, and the last rows, are compared."""
+    M, N, K = 150000, 256, 28672
+    rows_max = ((1 << 32) - 1) // K
+    rows_max -= rows_max % 256
+    assert M * K > (1 << 32) and rows_max < M
+    say(f"linear {M}x{K}->{N}, row block {rows_max}")
+    g = torch.Generator(device="cuda").manual_seed(77)
+    x_d = torch.randn((M, K), generator=g, device="cuda", dtype=torch.bfloat16)
+    wb = synth.weights(N, K, 4242)
+    w_d = dev_bf16(wb)
+    qw_d, sw_d = F.fp8_quant_act(w_d)
+    y_d, qx_d, sx_d = F.fp8_linear(x_d, qw_d, sw_d)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([sample_idx(M, 24, 78),
+                                     np.arange(rows_max - 3, rows_max + 3), np.arange(M - 3, M)]))
+    rows_d = torch.from_numpy(rows).cuda()
+    xb = host_bits(x_d[rows_d])
+    del x_d
+    qx_o, sx_o = O.quant_per_row(xb)
+    assert_codes_equal(qx_d[rows_d].cpu().numpy(), qx_o, "act codes")
+    assert_scales_equal(sx_d[rows_d].cpu().numpy(), sx_o, "act scales")
+    qw_o, sw_o = O.quant_per_row(wb)
+    assert_y_close(host_bf16_f64(y_d[rows_d]), O.linear_per_channel(qx_o, sx_o, qw_o, sw_o), "y")
+
+
 # ----------------------------------------------------------------------------
 # The whole linear on the workloads
 # ----------------------------------------------------------------------------
@@ -343,7 +388,7 @@ def test_c5_full_size_sampled(F):
 # ----------------------------------------------------------------------------
 DECODE_CASES = [(1, 8192, 8192), (5, 100, 1664), (16, 1024, 4096), (17, 520, 3200),
                 (33, 4096, 896), (64, 10240, 8192), (64, 33, 128), (2, 2048, 28672),
-                (8, 57344, 8192)]
+                (8, 57344, 8192), (48, 1000, 1152), (50, 130, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", DECODE_CASES)
