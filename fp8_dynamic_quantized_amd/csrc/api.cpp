@@ -49,8 +49,9 @@ int check_gemm_args(const uint8_t* qx, const float* sx, const uint8_t* qw,
   if (block && (N % 128) != 0) return FP8DQ_ERR_SHAPE;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return FP8DQ_ERR_SHAPE;
   if (!known_flags(flags)) return FP8DQ_ERR_FLAGS;
-  // prefill: the weight operand is addressed with 32-bit byte offsets
-  if (!use_decode(M, flags) && N * K >= (int64_t(1) << 32)) return FP8DQ_ERR_SHAPE;
+  // the prefill and whole-line decode kernels address the weight operand
+  // with 32-bit byte offsets
+  if (N * K >= (int64_t(1) << 32)) return FP8DQ_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8DQ_OK;
   if (!qx || !sx || !qw || !sw || !y) return FP8DQ_ERR_NULL;
   if (!aligned16(qx) || !aligned16(sx) || !aligned16(qw) || !aligned16(sw) ||

@@ -497,6 +497,8 @@ DecodePlan plan_decode(int64_t M, int64_t N, int64_t K) {
 #else
   p.line = M > 16 ? 1 : 0;
 #endif
+  // the whole-line kernel addresses token rows with 32-bit byte offsets
+  if ((int64_t)M * K >= (int64_t(1) << 32)) p.line = 0;
   if (p.line) {
     // Whole-line kernel: 128 weight rows per workgroup, two workgroups per
     // CU. Split K until there are >= 384 workgroups (1.5 per CU), keeping at

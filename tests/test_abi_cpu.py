@@ -72,9 +72,11 @@ def test_gemm_errors(L, fn):
     assert g(A, A, MIS, A, A, 100, 128, 128, 1, None, 0, None) == -3
     assert g(A, A, A, A, A, 0, 128, 128, 0, None, 0, None) == 0     # empty M
     assert g(None, None, None, None, None, 16, 0, 128, 0, None, 0, None) == 0
-    # prefill path: weight codes must stay under 4 GiB (32-bit offsets)
+    # weight codes must stay under 4 GiB (32-bit offsets), on every path
     assert g(A, A, A, A, A, 128, 1 << 16, 1 << 16, 0, None, 0, None) == -2
     assert g(A, A, A, A, A, 16, 1 << 16, 1 << 16, 1, None, 0, None) == -2
+    assert g(A, A, A, A, A, 32, 1 << 16, 1 << 16, 0, None, 0, None) == -2
+    assert g(A, A, A, A, A, 1, 1 << 16, 1 << 16, 2, None, 0, None) == -2
 
 
 def test_gemm_block_needs_n_multiple_of_128(L):
