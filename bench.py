@@ -127,13 +127,14 @@ def cpu_baseline(shapes, rows, col_frac):
                       f"quantization before timing; host cores {os.cpu_count()}"}
 
 
-def bench_prefill(F, torch, steps, warmup):
+def bench_prefill(F, torch, steps, warmup, only=None):
     import synth
-    shapes = synth.SHAPES["c2"]
+    shapes = [s for s in synth.SHAPES["c2"] if only is None or s[0] in only]
     M = synth.M_OF["c2"][0]
     log(f"prefill setup: {len(shapes)} linears, M={M}")
     layers = []
-    for j, (name, K, N) in enumerate(shapes):
+    for name, K, N in shapes:
+        j = [s[0] for s in synth.SHAPES["c2"]].index(name)
         d = synth.workload(2, j)
         x = to_dev(d["x"], torch)
         w = to_dev(d["w"], torch)
@@ -437,6 +438,10 @@ def main():
                     help="skip the block-variant section (Llama-3.2-3B shapes)")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the fused-producer / calibration / KV-cache section")
+    ap.add_argument("--linears", default="qkv,o,gate_up,down",
+                    help="prefill linears to run (profiling runs that must tell "
+                         "the gate_up launches apart: every per-channel linear "
+                         "of this size launches the same grid); must include gate_up")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-profile", metavar="DIR")
     args = ap.parse_args()
@@ -466,7 +471,11 @@ def main():
     F.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
-    pre = bench_prefill(F, torch, args.steps, args.warmup)
+    only = [s.strip() for s in args.linears.split(",") if s.strip()]
+    if "gate_up" not in only:
+        print("bench.py: --linears must include gate_up (the roofline kernel)", file=sys.stderr)
+        sys.exit(2)
+    pre = bench_prefill(F, torch, args.steps, args.warmup, only)
     M, K, N = pre["dom_shape"]
     out = {
         "metric": METRIC,

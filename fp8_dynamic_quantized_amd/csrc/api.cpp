@@ -50,8 +50,9 @@ int check_gemm_args(const uint8_t* qx, const float* sx, const uint8_t* qw,
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return FP8DQ_ERR_SHAPE;
   if (!known_flags(flags)) return FP8DQ_ERR_FLAGS;
   // the prefill and whole-line decode kernels address the weight operand
-  // with 32-bit byte offsets
-  if (N * K >= (int64_t(1) << 32)) return FP8DQ_ERR_SHAPE;
+  // with 32-bit byte offsets, and the prefill path runs X in blocks of whole
+  // 256-row tiles that fit them (K < 2^24)
+  if (N * K >= (int64_t(1) << 32) || K >= (int64_t(1) << 24)) return FP8DQ_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8DQ_OK;
   if (!qx || !sx || !qw || !sw || !y) return FP8DQ_ERR_NULL;
   if (!aligned16(qx) || !aligned16(sx) || !aligned16(qw) || !aligned16(sw) ||
@@ -77,6 +78,7 @@ int run_gemm(const uint8_t* qx, const float* sx, const uint8_t* qw,
     const int64_t G = K / 128;
     int64_t rows_max = ((int64_t(1) << 32) - 1) / K;
     rows_max -= rows_max % 256;
+    if (rows_max <= 0) return FP8DQ_ERR_SHAPE;   // excluded by the size rules
     for (int64_t m0 = 0; m0 < M; m0 += rows_max) {
       const int64_t rows = (M - m0) < rows_max ? (M - m0) : rows_max;
       fp8dq::launch_gemm_prefill(qx + m0 * K, sx + (block ? m0 * G : m0), qw, sw,

@@ -111,8 +111,8 @@ int fp8_quant_weight_block(const void* w_bf16, int64_t N, int64_t K,
  *   flags : FP8DQ_AUTO / FP8DQ_FORCE_PREFILL / FP8DQ_FORCE_DECODE
  *   ws, ws_bytes : device workspace for split-K partial sums; ws may be
  *        NULL iff fp8_workspace_bytes(M, N, K, 0, flags) == 0.
- * Size rules: M, N >= 0; K > 0 and K % 128 == 0; N * K < 2^32 (the
- * weight codes under 4 GiB; FP8DQ_ERR_SHAPE otherwise).
+ * Size rules: M, N >= 0; K > 0, K % 128 == 0 and K < 2^24; N * K < 2^32
+ * (the weight codes under 4 GiB); FP8DQ_ERR_SHAPE otherwise.
  */
 int fp8_gemm(const uint8_t* qx, const float* sx, const uint8_t* qw,
              const float* sw, void* y_bf16, int64_t M, int64_t N, int64_t K,
@@ -123,8 +123,8 @@ int fp8_gemm(const uint8_t* qx, const float* sx, const uint8_t* qw,
  *   y[m,n] = bf16( sum_g P_g[m,n] * sx[m,g] * sw[n/128, g] ), P_g the code
  *   product summed over the g-th 128-column group.
  *   sx : fp32 [M, K/128];  sw : fp32 [N/128, K/128]
- * Size rules: M, N >= 0; N % 128 == 0; K > 0 and K % 128 == 0;
- * N * K < 2^32, as for fp8_gemm.
+ * Size rules: M, N >= 0; N % 128 == 0; K > 0, K % 128 == 0 and
+ * K < 2^24; N * K < 2^32, as for fp8_gemm.
  * ws as for fp8_gemm (block = 1 in fp8_workspace_bytes).
  */
 int fp8_gemm_block(const uint8_t* qx, const float* sx, const uint8_t* qw,

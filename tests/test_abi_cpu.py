@@ -77,6 +77,9 @@ def test_gemm_errors(L, fn):
     assert g(A, A, A, A, A, 16, 1 << 16, 1 << 16, 1, None, 0, None) == -2
     assert g(A, A, A, A, A, 32, 1 << 16, 1 << 16, 0, None, 0, None) == -2
     assert g(A, A, A, A, A, 1, 1 << 16, 1 << 16, 2, None, 0, None) == -2
+    # K from 2^24 (a 256-row block of X codes would pass 4 GiB)
+    assert g(A, A, A, A, A, 65536, 128, 1 << 24, 0, None, 0, None) == -2
+    assert g(A, A, A, A, A, 16, 128, 1 << 24, 0, None, 0, None) == -2
 
 
 def test_gemm_block_needs_n_multiple_of_128(L):

@@ -207,6 +207,25 @@ def test_gemm_wide_tiles_ragged(F, M, N, K):
     assert_y_close(host_bf16_f64(y), O.linear_per_channel(qx, sx, qw, sw), "y")
 
 
+@pytest.mark.parametrize("M,N,K", [(4352, 4096, 384), (4200, 2176, 1152), (2100, 4352, 512)])
+def test_gemm_block_wide_tiles(F, M, N, K):
+    """Block-scaled GEMM with more tiles than CUs (workgroups walk several
+    tiles), ragged M, the shortest K of that mode (three groups), and
+    group scales that differ by orders of magnitude between groups."""
+    say(f"gemm block wide {M}x{N}x{K}")
+    G = K // 128
+    rng = np.random.default_rng(M + 3 * N + K)
+    qx = rng.choice(FINITE, size=(M, K))
+    qw = rng.choice(FINITE, size=(N, K))
+    sx = (rng.uniform(0.5, 1.0, (M, G)) * 10.0 ** rng.integers(-6, -2, (M, G))).astype(np.float32)
+    sw = (rng.uniform(0.5, 1.0, (N // 128, G)) * 10.0 ** rng.integers(-5, -2, (N // 128, G))).astype(np.float32)
+    qx[7, 128:256] = 0                                 # an all-zero activation group
+    sx[7, 1] = 0.0
+    y = F.fp8_gemm_block(dev(qx), dev(sx), dev(qw), dev(sw), flags=1)
+    torch.cuda.synchronize()
+    assert_y_close(host_bf16_f64(y), O.linear_block(qx, sx, qw, sw), "y")
+
+
 def test_linear_x_beyond_4gib(F):
     """fp8_linear with M * K > 2^32 bytes of X codes: the prefill path runs
     row blocks so that each block's operand offsets fit 32 bits; rows on
