@@ -359,75 +359,109 @@ __device__ __forceinline__ uint32_t okey_inv(uint32_t k) {
 }
 
 constexpr int kHistBlocks = 1024;
+constexpr int kSub = 16;   // sub-histograms per block, by lane % 16
 
-// Pass 1: per-block histogram of the key's high byte. Pass 2: per-block
-// histograms of the low byte of the keys whose high byte is sel[0] / sel[2].
+// The two global histograms (256 high-byte, 512 low-byte counters) start at 0.
+__global__ __launch_bounds__(256) void calib_zero_kernel(unsigned long long* __restrict__ hist) {
+  for (int i = threadIdx.x; i < 768; i += 256) hist[i] = 0ull;
+}
+
+// Pass 1: histogram of the key's high byte. Pass 2: histograms of the low
+// byte of the keys whose high byte is sel[0] / sel[2]. Each block counts
+// into kSub sub-histograms laid out [bin][sub]: the lanes of one wave that
+// hit the same bin use different banks (at most 4 lanes share a sub), where
+// one histogram serialised up to 64 lanes on the few populated buckets of
+// real data. Blocks then add their counts to the global histogram (integer
+// atomics: the sums are exact and order-free).
 template <bool SECOND>
 __global__ __launch_bounds__(256) void calib_hist_kernel(const uint4* __restrict__ x,
                                                          int64_t nch, const int64_t* sel,
-                                                         uint32_t* __restrict__ part) {
-  __shared__ uint32_t hst[SECOND ? 512 : 256];
+                                                         unsigned long long* __restrict__ hist) {
+  constexpr int NB = SECOND ? 512 : 256;
+  __shared__ uint32_t hst[NB * kSub];
   const int tid = threadIdx.x;
-  for (int b = tid; b < (SECOND ? 512 : 256); b += 256) hst[b] = 0;
+  const uint32_t sub = (uint32_t)tid & (kSub - 1);
+  for (int b = tid; b < NB * kSub; b += 256) hst[b] = 0;
   uint32_t hb_lo = 0, hb_hi = 0;
   if (SECOND) { hb_lo = (uint32_t)sel[0]; hb_hi = (uint32_t)sel[2]; }
   __syncthreads();
-  for (int64_t c = (int64_t)blockIdx.x * 256 + tid; c < nch; c += (int64_t)gridDim.x * 256) {
-    const uint4 v = ld16(x + c);
+  auto count = [&](const uint4 v) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t k = okey((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
       if (!SECOND) {
-        atomicAdd(&hst[k >> 8], 1u);
+        atomicAdd(&hst[(k >> 8) * kSub + sub], 1u);
       } else {
-        if ((k >> 8) == hb_lo) atomicAdd(&hst[k & 255u], 1u);
-        if ((k >> 8) == hb_hi) atomicAdd(&hst[256 + (k & 255u)], 1u);
+        if ((k >> 8) == hb_lo) atomicAdd(&hst[(k & 255u) * kSub + sub], 1u);
+        if ((k >> 8) == hb_hi) atomicAdd(&hst[(256 + (k & 255u)) * kSub + sub], 1u);
       }
     }
+  };
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t c = (int64_t)blockIdx.x * 256 + tid;
+  for (; c + 3 * stride < nch; c += 4 * stride) {   // four loads in flight
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = ld16(x + c + u * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) count(v[u]);
   }
+  for (; c < nch; c += stride) count(ld16(x + c));
   __syncthreads();
-  for (int b = tid; b < (SECOND ? 512 : 256); b += 256)
-    part[(int64_t)blockIdx.x * (SECOND ? 512 : 256) + b] = hst[b];
+  for (int b = tid; b < NB; b += 256) {
+    uint32_t t = 0;   // a block counts below 2^30 values (n < 2^40, 1024 blocks)
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) t += hst[b * kSub + u];
+    if (t) atomicAdd(&hist[(SECOND ? 256 : 0) + b], (unsigned long long)t);
+  }
 }
 
-// Sum the per-block histograms (fixed order) and find, for ranks k_lo and
-// k_hi (1-based), the bucket and the rank inside it. One block of 256.
-// SECOND: the buckets are low bytes; write the scale.
+// For ranks k_lo and k_hi (1-based), the bucket holding the rank and the
+// rank inside it, from inclusive prefix sums of the histogram. One block of
+// 256. SECOND: the buckets are low bytes; write the scale.
 template <bool SECOND>
-__global__ __launch_bounds__(256) void calib_select_kernel(const uint32_t* __restrict__ part,
-                                                           int nblk, int64_t k_lo, int64_t k_hi,
+__global__ __launch_bounds__(256) void calib_select_kernel(const unsigned long long* __restrict__ hist,
+                                                           int64_t k_lo, int64_t k_hi,
                                                            int64_t* sel, float* scale_out) {
-  __shared__ int64_t cnt[2][256];
+  constexpr int H = SECOND ? 2 : 1;
+  __shared__ int64_t cnt[H][256], inc[H][256];
+  __shared__ int64_t res[4];
   const int tid = threadIdx.x;
-  constexpr int W = SECOND ? 512 : 256;
-  for (int h = 0; h < (SECOND ? 2 : 1); ++h) {
-    int64_t s = 0;
-    for (int b = 0; b < nblk; ++b) s += part[(int64_t)b * W + h * 256 + tid];
-    cnt[h][tid] = s;
+  for (int h = 0; h < H; ++h) {
+    const int64_t c = (int64_t)hist[(SECOND ? 256 : 0) + h * 256 + tid];
+    cnt[h][tid] = c;
+    inc[h][tid] = c;
+  }
+  const int64_t ranks[2] = {SECOND ? sel[1] : k_lo, SECOND ? sel[3] : k_hi};
+  if (tid < 4) res[tid] = (tid & 1) ? ranks[tid >> 1] : 0;   // k = 0: bucket 0, rank 0
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {
+    int64_t t[H];
+#pragma unroll
+    for (int h = 0; h < H; ++h) t[h] = tid >= d ? inc[h][tid - d] : 0;
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < H; ++h) inc[h][tid] += t[h];
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int h = SECOND ? j : 0;
+    const int64_t k = ranks[j];
+    const int64_t before = inc[h][tid] - cnt[h][tid];
+    if (k >= 1 && before < k && k <= inc[h][tid]) {   // exactly one bucket
+      res[2 * j] = tid;
+      res[2 * j + 1] = k - before;
+    }
   }
   __syncthreads();
   if (tid == 0) {
-    int64_t ranks[2] = {k_lo, k_hi};
-    int64_t out[4];
-    for (int j = 0; j < 2; ++j) {
-      const int h = SECOND ? j : 0;
-      int64_t k = SECOND ? sel[2 * j + 1] : ranks[j];
-      int b = 0;
-      int64_t before = 0;
-      for (; b < 256; ++b) {
-        if (before + cnt[h][b] >= k) break;
-        before += cnt[h][b];
-      }
-      if (b > 255) b = 255;   // empty input (k = 0 cannot be reached otherwise)
-      out[2 * j] = b;
-      out[2 * j + 1] = k - before;
-    }
     if (!SECOND) {
-      for (int j = 0; j < 4; ++j) sel[j] = out[j];
+      for (int j = 0; j < 4; ++j) sel[j] = res[j];
     } else {
-      const uint32_t key_lo = ((uint32_t)sel[0] << 8) | (uint32_t)out[0];
-      const uint32_t key_hi = ((uint32_t)sel[2] << 8) | (uint32_t)out[2];
+      const uint32_t key_lo = ((uint32_t)sel[0] << 8) | (uint32_t)res[0];
+      const uint32_t key_hi = ((uint32_t)sel[2] << 8) | (uint32_t)res[2];
       const float vlo = fabsf(__uint_as_float(okey_inv(key_lo) << 16));
       const float vhi = fabsf(__uint_as_float(okey_inv(key_hi) << 16));
       const float amax = (k_hi > 0) ? fmaxf(vlo, vhi) : 0.0f;
@@ -617,7 +651,7 @@ int launch_kv_quant(const void* x, int64_t T, int64_t width, const int64_t* slot
 }
 
 size_t calib_workspace_bytes() {
-  return (size_t)kHistBlocks * (256 + 512) * 4 + 4 * sizeof(int64_t);
+  return 768 * sizeof(unsigned long long) + 4 * sizeof(int64_t);
 }
 
 void launch_calib_scale(const void* x, int64_t n, int64_t k_lo, int64_t k_hi,
@@ -626,17 +660,17 @@ void launch_calib_scale(const void* x, int64_t n, int64_t k_lo, int64_t k_hi,
   int nblk = (int)((nch + 255) / 256);
   if (nblk > kHistBlocks) nblk = kHistBlocks;
   if (nblk < 1) nblk = 1;
-  uint32_t* part1 = static_cast<uint32_t*>(ws);
-  uint32_t* part2 = part1 + (size_t)kHistBlocks * 256;
-  int64_t* sel = reinterpret_cast<int64_t*>(part2 + (size_t)kHistBlocks * 512);
+  unsigned long long* hist = static_cast<unsigned long long*>(ws);
+  int64_t* sel = reinterpret_cast<int64_t*>(hist + 768);
+  hipLaunchKernelGGL(calib_zero_kernel, dim3(1), dim3(256), 0, st, hist);
   hipLaunchKernelGGL((calib_hist_kernel<false>), dim3(nblk), dim3(256), 0, st,
-                     (const uint4*)x, nch, (const int64_t*)sel, part1);
+                     (const uint4*)x, nch, (const int64_t*)sel, hist);
   hipLaunchKernelGGL((calib_select_kernel<false>), dim3(1), dim3(256), 0, st,
-                     (const uint32_t*)part1, nblk, k_lo, k_hi, sel, scale_out);
+                     (const unsigned long long*)hist, k_lo, k_hi, sel, scale_out);
   hipLaunchKernelGGL((calib_hist_kernel<true>), dim3(nblk), dim3(256), 0, st,
-                     (const uint4*)x, nch, (const int64_t*)sel, part2);
+                     (const uint4*)x, nch, (const int64_t*)sel, hist);
   hipLaunchKernelGGL((calib_select_kernel<true>), dim3(1), dim3(256), 0, st,
-                     (const uint32_t*)part2, nblk, k_lo, k_hi, sel, scale_out);
+                     (const unsigned long long*)hist, k_lo, k_hi, sel, scale_out);
 }
 
 void launch_quant_static(const void* x, int64_t n, const float* scale, uint8_t* q,

@@ -116,6 +116,25 @@ def test_calib_scale(F, n, lo, hi):
     assert_scales_equal(s.cpu().numpy(), np.array([want], np.float32), "calib scale")
 
 
+@pytest.mark.parametrize("n_ext", [7, 8, 9])
+def test_calib_scale_rank_at_bucket_edges(F, n_ext):
+    """8000 values: n_ext of them -3.0, one -0.0 and one +0.0, the rest 1.0
+    (one key, so one bucket holds nearly every value): the P0.1 rank (k = 8)
+    lands inside, exactly at and just past the end of the -3.0 group, the
+    P99.9 rank inside the 1.0 group."""
+    n = 8000
+    x = np.full(n, 0x3F80, np.uint16)                  # 1.0
+    x[:n_ext] = 0xC040                                 # -3.0
+    x[n_ext] = 0x8000                                  # -0.0
+    x[n_ext + 1] = 0x0000                              # +0.0
+    x = np.random.default_rng(n_ext).permutation(x)
+    say(f"calib bucket edges n_ext={n_ext}")
+    s = F.fp8_calib_scale(dev_bf16(x), 1, 999)
+    torch.cuda.synchronize()
+    want = O.calib_scale(x, 1, 999)
+    assert_scales_equal(s.cpu().numpy(), np.array([want], np.float32), "calib scale")
+
+
 @pytest.mark.parametrize("n", [1 << 28, (1 << 32) + 8000])
 def test_calib_scale_closed_form_large(F, n):
     """n values cycling through 1000 distinct bf16 values: the nearest-rank
