@@ -285,11 +285,9 @@ int fp8_kv_cache_quant(const void* k_bf16, const void* v_bf16, int64_t T, int64_
       (reinterpret_cast<uintptr_t>(k_scale) & 3u) || (reinterpret_cast<uintptr_t>(v_scale) & 3u))
     return FP8DQ_ERR_ALIGN;
   hipStream_t st = as_stream(stream);
-  if (fp8dq::launch_kv_quant(k_bf16, T, width, slots, n_slots, k_cache, k_scale, st) != 0)
+  if (fp8dq::launch_kv_quant(k_bf16, v_bf16, T, width, slots, n_slots, k_cache, v_cache,
+                             k_scale, v_scale, st) != 0)
     return FP8DQ_ERR_SHAPE;
-  int s = launch_status();
-  if (s != FP8DQ_OK) return s;
-  fp8dq::launch_kv_quant(v_bf16, T, width, slots, n_slots, v_cache, v_scale, st);
   return launch_status();
 }
 

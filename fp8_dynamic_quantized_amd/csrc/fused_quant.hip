@@ -524,15 +524,23 @@ __global__ __launch_bounds__(256) void quant_static_kernel(const uint4* __restri
 }
 
 // ---- FP8 KV cache: per-token quantization, rows scattered by slot ---------
+// One launch for K and V: rows 0 .. T-1 of the grid are K's tokens, T .. 2T-1
+// V's (a team takes one row).
 template <int CH, int TW>
 __global__ __launch_bounds__(TW >= 4 ? 64 * TW : 256) void kv_quant_kernel(
-    const uint4* __restrict__ x, int64_t T, int64_t width, const int64_t* __restrict__ slots,
-    int64_t n_slots, uint2* __restrict__ cache, float* __restrict__ cscale) {
+    const uint4* __restrict__ k, const uint4* __restrict__ v, int64_t T, int64_t width,
+    const int64_t* __restrict__ slots, int64_t n_slots, uint2* __restrict__ kc,
+    uint2* __restrict__ vc, float* __restrict__ ks, float* __restrict__ vs) {
   constexpr int TEAM = 64 * TW;
   constexpr int RPB = TW >= 4 ? 1 : 4 / TW;
   __shared__ uint32_t red[TW >= 4 ? TW : 4];
   const int tid = threadIdx.x, tl = tid % TEAM;
-  const int64_t t = (int64_t)blockIdx.x * RPB + tid / TEAM;
+  const int64_t t2 = (int64_t)blockIdx.x * RPB + tid / TEAM;
+  const bool is_v = t2 >= T;
+  const int64_t t = is_v ? t2 - T : t2;
+  const uint4* x = is_v ? v : k;
+  uint2* cache = is_v ? vc : kc;
+  float* cscale = is_v ? vs : ks;
   const int64_t nch = width >> 3;
   const int64_t slot = t < T ? slots[t] : -1;
   const bool row_ok = slot >= 0 && slot < n_slots;   // out-of-range slots are skipped
@@ -612,11 +620,13 @@ struct RmsLaunch {
 };
 template <int CH, int TW>
 struct KvLaunch {
-  static void go(const void* x, int64_t T, int64_t width, const int64_t* slots,
-                 int64_t n_slots, uint8_t* cache, float* cs, hipStream_t st) {
-    hipLaunchKernelGGL((kv_quant_kernel<CH, TW>), (RowsGrid<CH, TW>::blocks(T)),
-                       (RowsGrid<CH, TW>::threads()), 0, st, (const uint4*)x, T, width,
-                       slots, n_slots, (uint2*)cache, cs);
+  static void go(const void* k, const void* v, int64_t T, int64_t width, const int64_t* slots,
+                 int64_t n_slots, uint8_t* kc, uint8_t* vc, float* ks, float* vs,
+                 hipStream_t st) {
+    hipLaunchKernelGGL((kv_quant_kernel<CH, TW>), (RowsGrid<CH, TW>::blocks(2 * T)),
+                       (RowsGrid<CH, TW>::threads()), 0, st, (const uint4*)k,
+                       (const uint4*)v, T, width, slots, n_slots, (uint2*)kc, (uint2*)vc, ks,
+                       vs);
   }
 };
 
@@ -645,9 +655,11 @@ int launch_rmsnorm(const void* x, const void* gamma, int64_t rows, int64_t H, do
                                                           (float*)nullptr, st);
 }
 
-int launch_kv_quant(const void* x, int64_t T, int64_t width, const int64_t* slots,
-                    int64_t n_slots, uint8_t* cache, float* cscale, hipStream_t st) {
-  return launch_ladder<KvLaunch>(width / 8, x, T, width, slots, n_slots, cache, cscale, st);
+int launch_kv_quant(const void* k, const void* v, int64_t T, int64_t width,
+                    const int64_t* slots, int64_t n_slots, uint8_t* kc, uint8_t* vc,
+                    float* ks, float* vs, hipStream_t st) {
+  return launch_ladder<KvLaunch>(width / 8, k, v, T, width, slots, n_slots, kc, vc, ks, vs,
+                                 st);
 }
 
 size_t calib_workspace_bytes() {

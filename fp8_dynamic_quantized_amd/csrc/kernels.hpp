@@ -52,8 +52,9 @@ int launch_rmsnorm_quant(const void* x, const void* gamma, int64_t rows, int64_t
 int launch_silu_mul(const void* gu, int64_t rows, int64_t I, void* h, hipStream_t st);
 int launch_rmsnorm(const void* x, const void* gamma, int64_t rows, int64_t H, double eps,
                    void* h, hipStream_t st);
-int launch_kv_quant(const void* x, int64_t T, int64_t width, const int64_t* slots,
-                    int64_t n_slots, uint8_t* cache, float* cscale, hipStream_t st);
+int launch_kv_quant(const void* k, const void* v, int64_t T, int64_t width,
+                    const int64_t* slots, int64_t n_slots, uint8_t* kc, uint8_t* vc,
+                    float* ks, float* vs, hipStream_t st);
 size_t calib_workspace_bytes();
 void launch_calib_scale(const void* x, int64_t n, int64_t k_lo, int64_t k_hi,
                         float* scale_out, void* ws, hipStream_t st);
