@@ -49,7 +49,7 @@ sys.path.insert(0, ROOT)
 METRIC = "FP8-dynamic linear TFLOP/s (prefill) + weight GB/s (decode), % of roofline"
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
-DOM_KERNEL = "gemm_prefill_line_kernel<false>"
+DOM_KERNEL = "gemm_prefill_line_kernel<false, 256>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_prefill_line_gate_up_m4096_traffic.txt")
 KERNEL_SOURCES = ["fp8_dynamic_quantized_amd/csrc/gemm_line.hpp",
                   "fp8_dynamic_quantized_amd/csrc/gemm_prefill.hip",

@@ -11,7 +11,7 @@ namespace fp8dq {
 void launch_gemm_line_block(const uint8_t* qx, const float* sx, const uint8_t* qw,
                             const float* sw, void* y, int64_t M, int64_t N, int64_t K,
                             hipStream_t st) {
-  line::launch_line<true>(qx, sx, qw, sw, y, M, N, K, st);
+  line::launch_line<true, 128>(qx, sx, qw, sw, y, M, N, K, st);
 }
 
 }  // namespace fp8dq

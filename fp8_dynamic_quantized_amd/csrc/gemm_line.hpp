@@ -27,7 +27,7 @@ constexpr int GM = 8;  // tile rows per L2 group
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 // ---------------------------------------------------------------------------
-// Whole-line kernels: 256 x BN tiles (BN = 256 per-channel, 128 block),
+// Whole-line kernels: 256 x BN tiles (BN = 256 or 192 per-channel, 128 block),
 // v_mfma_f32_32x32x64_f8f6f4, 4 waves (2 x 2).
 //  * A load instruction moves 8 rows x 128 bytes (two 64-byte MFMA K steps of
 //    each row): every request is a whole 128-byte line. The L2 -> LDS path
@@ -64,9 +64,9 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 // ---------------------------------------------------------------------------
 constexpr int LBK = 128;                 // K bytes per pair (two MFMA steps)
 
-template <bool BLOCK>
+template <bool BLOCK, int BNP>
 struct LineCfg {
-  static constexpr int BM = 256, BN = BLOCK ? 128 : 256;
+  static constexpr int BM = 256, BN = BNP;
   static constexpr int NSL = BLOCK ? 3 : 2;                 // pair slots
   static constexpr int SLOT = (BM + BN) * LBK;
   static constexpr int XQ = BM / 32, WQ = BN / 32;          // loads per wave per pair
@@ -89,12 +89,13 @@ __device__ __forceinline__ uint32_t pk_bf16_rne(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-template <bool BLOCK>
+template <bool BLOCK, int BNP>
 __global__ __launch_bounds__(256, 1) void gemm_prefill_line_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint8_t* __restrict__ qw, const float* __restrict__ sw,
     uint16_t* __restrict__ y, int M, int N, int K, int tiles_m, int tiles_n) {
-  using C = LineCfg<BLOCK>;
+  using C = LineCfg<BLOCK, BNP>;
+  static_assert(BLOCK ? BNP == 128 : (BNP == 256 || BNP == 192), "tile widths built");
   constexpr int BM = C::BM, BN = C::BN, NSL = C::NSL, SLOT = C::SLOT;
   constexpr int XQ = C::XQ, WQ = C::WQ, NLD = C::NLD;
   constexpr int DTM = 128, DTN = BN / 2;
@@ -438,13 +439,22 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_line_kernel(
   }
 }
 
-template <bool BLOCK>
+// Compute units of the current device (0 when the runtime does not say).
+inline int cu_count() {
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return ncu;
+}
+
+template <bool BLOCK, int BNP>
 void launch_line(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
                  void* y, int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  using C = LineCfg<BLOCK>;
+  using C = LineCfg<BLOCK, BNP>;
   static std::once_flag once;
   std::call_once(once, [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_prefill_line_kernel<BLOCK>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_prefill_line_kernel<BLOCK, BNP>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   });
   const int tiles_m = (int)((M + C::BM - 1) / C::BM);
@@ -460,14 +470,11 @@ void launch_line(const uint8_t* qx, const float* sx, const uint8_t* qw, const fl
   int grid = ntiles;
 #if FP8DQ_LINE_PERSIST
   if (!BLOCK) {
-    int dev = 0, ncu = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        ncu > 0 && ncu % 8 == 0 && ntiles > ncu)
-      grid = ncu;
+    const int ncu = cu_count();
+    if (ncu > 0 && ncu % 8 == 0 && ntiles > ncu) grid = ncu;
   }
 #endif
-  hipLaunchKernelGGL((gemm_prefill_line_kernel<BLOCK>), dim3((unsigned)grid), dim3(256),
+  hipLaunchKernelGGL((gemm_prefill_line_kernel<BLOCK, BNP>), dim3((unsigned)grid), dim3(256),
                      C::smem(K), st, qx, sx, qw, sw, (uint16_t*)y, (int)M, (int)N, (int)K,
                      tiles_m, tiles_n);
 }

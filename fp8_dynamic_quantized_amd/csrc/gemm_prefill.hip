@@ -668,7 +668,22 @@ void launch_gemm_prefill(const uint8_t* qx, const float* sx, const uint8_t* qw,
 #elif defined(FP8DQ_TILE_OVERRIDE) && FP8DQ_TILE_OVERRIDE == 5
     launch_deep<256, 4, 1>(qx, sx, qw, sw, y, M, N, K, st);
 #else
-    if (use_big && K >= 256) line::launch_line<false>(qx, sx, qw, sw, y, M, N, K, st);
+    if (use_big && K >= 256) {
+      // 256 x 192 tiles when they fill the last round of tiles on the CUs
+      // better: the time goes as (rounds of tiles) x (tile width), and a
+      // shape like 4096 x 6144 has 1.5 rounds of 256-wide tiles but two full
+      // rounds of 192-wide ones
+      const int ncu = line::cu_count();
+      const int64_t tm = (M + 255) / 256;
+      const int64_t t256 = tm * ((N + 255) / 256), t192 = tm * ((N + 191) / 192);
+      bool narrow = false;
+      if (ncu > 0) {
+        const int64_t r256 = (t256 + ncu - 1) / ncu, r192 = (t192 + ncu - 1) / ncu;
+        narrow = r192 * 192 * 10 < r256 * 256 * 9;   // at least 10 % less
+      }
+      if (narrow) line::launch_line<false, 192>(qx, sx, qw, sw, y, M, N, K, st);
+      else line::launch_line<false, 256>(qx, sx, qw, sw, y, M, N, K, st);
+    }
     else if (use_big) launch_deep<256, 5, 1>(qx, sx, qw, sw, y, M, N, K, st);
     else launch_cfg<256, 128, false>(qx, sx, qw, sw, y, M, N, K, st);
 #endif

@@ -190,7 +190,15 @@ def test_gemm_random_codes_small_k(F):
                        f"random codes {M}x{N}x{K} flags={flags}")
 
 
-@pytest.mark.parametrize("M,N,K", [(4173, 3853, 384), (4097, 4104, 256), (4352, 4096, 1152)])
+WIDE_RAGGED = [
+    # 256 x 192 tiles (two full rounds of them against 1.1 - 1.5 rounds of 256-wide ones)
+    (4173, 3853, 384), (4097, 4104, 256), (4352, 4096, 1152), (4352, 4790, 384),
+    (4000, 6144, 256),
+    # 256 x 256 tiles: one round; two rounds with two workgroups taking one tile
+    (4000, 3990, 384), (4352, 7630, 256)]
+
+
+@pytest.mark.parametrize("M,N,K", WIDE_RAGGED)
 def test_gemm_wide_tiles_ragged(F, M, N, K):
     """Shapes with at least 256 tiles of 256 x 256 (the whole-line kernel)
     and ragged edges: M and N off the tile grid, N % 8 != 0 (element
