@@ -37,7 +37,7 @@ def sample_idx(n, k, seed):
 # ----------------------------------------------------------------------------
 ROW_SHAPES = [(1, 8), (3, 40), (5, 512), (7, 520), (64, 4096), (33, 3072),
               (17, 8192), (9, 14336), (5, 28672), (3, 40960), (2, 65536),
-              (130, 1024)]
+              (130, 1024), (300, 2056), (129, 3000), (200, 4096)]
 
 
 @pytest.mark.parametrize("rows,K", ROW_SHAPES)
@@ -415,7 +415,11 @@ def test_c5_full_size_sampled(F):
 # ----------------------------------------------------------------------------
 DECODE_CASES = [(1, 8192, 8192), (5, 100, 1664), (16, 1024, 4096), (17, 520, 3200),
                 (33, 4096, 896), (64, 10240, 8192), (64, 33, 128), (2, 2048, 28672),
-                (8, 57344, 8192), (48, 1000, 1152), (50, 130, 256)]
+                (8, 57344, 8192), (48, 1000, 1152), (50, 130, 256),
+                # split-K with one row, ragged N, 16 rows, the shortest K, the
+                # longest K at one row
+                (1, 64, 8192), (3, 100, 2048), (16, 200, 1920), (4, 32, 128),
+                (1, 8192, 28672)]
 
 
 @pytest.mark.parametrize("M,N,K", DECODE_CASES)
@@ -441,6 +445,30 @@ def test_decode_linear_shapes(F, M, N, K):
     cols_d = torch.from_numpy(cols).cuda()
     assert_y_close(host_bf16_f64(y[:, cols_d]),
                    O.linear_per_channel(qx_o, sx_o, qw_o, sw_o), "y")
+    y2 = F.fp8_gemm(qx, sx, qw_d, sw_d, flags=F.FORCE_DECODE)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "linear vs two-step"
+
+
+def test_decode_linear_special_rows(F):
+    """fp8_linear on the decode path with an all-zero row (scale 0), a row
+    whose scale needs the 2^64 pre-scale, a row of -0.0 and an ordinary row:
+    codes and scales bit-exact, y as the two-step path."""
+    M, N, K = 4, 300, 1024
+    xb = synth.activations(M, K, 1500, 1501)
+    xb[0] = 0
+    xb[1] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(xb[1]) * np.float32(2.0 ** -100))
+    xb[2] = 0x8000
+    wb = synth.weights(N, K, 1502)
+    qw_d, sw_d = F.fp8_quant_act(dev_bf16(wb))
+    y, qx, sx = F.fp8_linear(dev_bf16(xb), qw_d, sw_d)
+    torch.cuda.synchronize()
+    qx_o, sx_o = O.quant_per_row(xb)
+    assert sx_o[0] == 0 and 0 < sx_o[1] < 2.0 ** -64
+    assert_scales_equal(sx.cpu().numpy(), sx_o, "act scales")
+    assert_codes_equal(qx.cpu().numpy(), qx_o, "act codes")
+    qw_o, sw_o = O.quant_per_row(wb)
+    assert_y_close(host_bf16_f64(y), O.linear_per_channel(qx_o, sx_o, qw_o, sw_o), "y")
     y2 = F.fp8_gemm(qx, sx, qw_d, sw_d, flags=F.FORCE_DECODE)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "linear vs two-step"
