@@ -226,10 +226,11 @@ void launch_quant_rows(const void* x, int64_t rows, int64_t K, uint8_t* q,
     else launch_rows<4, 16>(x, rows, K, q, scale, st);
     return;
   }
-  // One wave per row for short rows, else a team of 4 waves. At K = 4096
-  // (512 chunks) the team is faster than one wave with 8 chunks per lane:
-  // 16.7 against 21.0 us on 4096 rows from HBM (the row's loads spread over
-  // 4 waves, and its amax / codes chain is 4 times shorter per lane).
+  // One wave per row for short rows, else a team of 4 (or 8) waves. At
+  // K = 4096 (512 chunks) the team is faster than one wave with 8 chunks per
+  // lane: 16.7 against 21.0 us on 4096 rows from HBM (the row's loads spread
+  // over 4 waves, and its amax / codes chain is 4 times shorter per lane);
+  // at K = 14336, 8 waves with 4 chunks each: 38 against 40 us.
   if (nch <= 64 * 1) launch_rows<1, 1>(x, rows, K, q, scale, st);
   else if (nch <= 64 * 2) launch_rows<2, 1>(x, rows, K, q, scale, st);
   else if (nch <= 64 * 4) launch_rows<4, 1>(x, rows, K, q, scale, st);
@@ -237,7 +238,7 @@ void launch_quant_rows(const void* x, int64_t rows, int64_t K, uint8_t* q,
   else if (nch <= 256 * 3) launch_rows<3, 4>(x, rows, K, q, scale, st);
   else if (nch <= 256 * 4) launch_rows<4, 4>(x, rows, K, q, scale, st);
   else if (nch <= 256 * 6) launch_rows<6, 4>(x, rows, K, q, scale, st);
-  else if (nch <= 256 * 8) launch_rows<8, 4>(x, rows, K, q, scale, st);
+  else if (nch <= 256 * 8) launch_rows<4, 8>(x, rows, K, q, scale, st);
   else if (nch <= 256 * 12) launch_rows<12, 4>(x, rows, K, q, scale, st);
   else if (nch <= 256 * 16) launch_rows<16, 4>(x, rows, K, q, scale, st);
   else

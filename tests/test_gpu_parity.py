@@ -37,7 +37,7 @@ def sample_idx(n, k, seed):
 # ----------------------------------------------------------------------------
 ROW_SHAPES = [(1, 8), (3, 40), (5, 512), (7, 520), (64, 4096), (33, 3072),
               (17, 8192), (9, 14336), (5, 28672), (3, 40960), (2, 65536),
-              (130, 1024), (300, 2056), (129, 3000), (200, 4096)]
+              (130, 1024), (300, 2056), (129, 3000), (200, 4096), (140, 14336), (130, 16384)]
 
 
 @pytest.mark.parametrize("rows,K", ROW_SHAPES)
