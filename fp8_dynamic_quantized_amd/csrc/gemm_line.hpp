@@ -22,6 +22,9 @@ constexpr int GM = 8;  // tile rows per L2 group
 #ifndef FP8DQ_LINE_PERSIST
 #define FP8DQ_LINE_PERSIST 1
 #endif
+#ifndef FP8DQ_LINE_EARLY
+#define FP8DQ_LINE_EARLY 1
+#endif
 // s_waitcnt immediate (gfx9 encoding): at most n vector-memory operations of
 // this wave outstanding (expcnt / lgkmcnt not waited on).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
@@ -296,12 +299,30 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_line_kernel(
   // next pair, barrier, read step kt+1 from the next slot, refill this
   // pair's slot with pair kt/2 + NSL; block: form the next group's rescale.
   // The first step of a tile starts its accumulators from zero.
+  //
+  // 256 x 192 tiles (EARLY): the refill moves to the middle of the even step
+  // and the wait for the next pair to the middle of the odd step, so a pair
+  // is issued about three K steps before it is read instead of two (waiting
+  // for the ring is the loop's largest stall). Even step: reads of the
+  // pair's second half, then (this wave's reads done, barrier: every wave's
+  // reads of the slot done) the refill of the pair's own slot with pair
+  // kt/2 + NSL. Odd step: the first half of the MFMAs, then the wait for
+  // the next pair (the pair issued after it may stay in flight), a barrier
+  // (every wave's part of it landed), and its first-half reads. Measured:
+  // 8B qkv 96 against 101 us; with 256-wide tiles the second barrier per
+  // pair costs more than the earlier refill gains (gate_up 400 against 388).
+  constexpr bool EARLY = !BLOCK && BNP == 192 && FP8DQ_LINE_EARLY;
+  constexpr int TB = (NR + 1) / 2;                          // even: reads before the barrier
+  constexpr int IPE = (NLD + NSC + (NM - TB) - 1) / (NM - TB);  // loads per slot after it
+  constexpr int TW = NM / 2;                                // odd: MFMAs before the wait
+  constexpr int RPO = (NR + (NM - TW) - 1) / (NM - TW);     // reads per slot after it
+  static_assert(TB < NM && TW < NM, "mid-step points inside the step");
   auto step = [&](int kt, auto cur_c, auto more_c, auto first_c) {
     constexpr int cur = decltype(cur_c)::value;
     constexpr bool more = decltype(more_c)::value;
     constexpr bool first = decltype(first_c)::value;
     const int ns = cs + 1 == NSL ? 0 : cs + 1;
-    if (cur == 1 && more) {
+    if (!EARLY && cur == 1 && more) {
       // vmcnt: the NSL-2 newer pairs may stay in flight; lgkmcnt(0): this
       // wave's reads of the slot refilled below are done
       __builtin_amdgcn_s_waitcnt(vmcnt_imm((NSL - 2) * (NLD + NSC)) & ~0x0F00);
@@ -319,6 +340,31 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_line_kernel(
           for (int u = 0; u < 2; ++u) {
             const int r = 2 * t + u;
             if (r < NR) read_frag(oA, oB, A[1], B[1], rs, 1, frag_of(r >> 1), r & 1);
+          }
+          if constexpr (EARLY) {
+            if (t == TB) {
+              __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+              asm volatile("s_barrier" ::: "memory");
+            }
+            if (t >= TB) {
+#pragma unroll
+              for (int u = 0; u < IPE; ++u) {
+                const int w = IPE * (t - TB) + u;
+                if (w < NLD + NSC) issue(cs, kt / 2 + NSL, w);
+              }
+            }
+          }
+        } else if constexpr (EARLY) {
+          if (t == TW) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm((NSL - 1) * (NLD + NSC)));
+            asm volatile("s_barrier" ::: "memory");
+          }
+          if (t >= TW) {
+#pragma unroll
+            for (int u = 0; u < RPO; ++u) {
+              const int r = RPO * (t - TW) + u;
+              if (r < NR) read_frag(oA, oB, A[0], B[0], rs, 0, frag_of(r >> 1), r & 1);
+            }
           }
         } else {
 #pragma unroll
