@@ -41,8 +41,8 @@ __device__ __forceinline__ bool near_mid16(float h) {
   return (low - (0x8000u - kMidTol)) <= 2u * kMidTol;
 }
 
-__device__ __forceinline__ bool tiny32(float h) {  // |h| < 2^-100
-  return (__float_as_uint(h) & 0x7FFFFFFFu) < 0x0D800000u;
+__device__ __forceinline__ bool tiny32(float h) {  // |h| < 2^-100 (one compare, |h| operand)
+  return __builtin_fabsf(h) < 0x1p-100f;
 }
 
 // Value of bf16 bit pattern b (sign included) as a double; b's magnitude may
@@ -232,9 +232,14 @@ __device__ __forceinline__ void quantize_team(const uint4 (&h)[CH], bool row_ok,
                                               int64_t nch, int team_lane, uint32_t* red,
                                               uint2* __restrict__ q, float* __restrict__ scale) {
   constexpr int TEAM = 64 * TW;
+  // chunks past the row end hold arbitrary values (their loads were not
+  // zeroed) and are left out here and at the store
   us2 m2 = {0, 0};
 #pragma unroll
-  for (int i = 0; i < CH; ++i) m2 = chunk_amax(h[i], m2);
+  for (int i = 0; i < CH; ++i) {
+    const us2 a = chunk_amax(h[i], m2);
+    if ((int64_t)i * TEAM + team_lane < nch) m2 = a;
+  }
   uint32_t m = m2.x > m2.y ? m2.x : m2.y;
   m = wave_max_u32(m);
   if (TW > 1) {   // the team's waves meet in red[team * TW ...]
@@ -286,11 +291,14 @@ __global__ __launch_bounds__(TW >= 4 ? 64 * TW : 256) void silu_mul_kernel(
   const bool row_ok = row < rows;
   const uint4* gr = gu + (row_ok ? row : 0) * 2 * nch;
   uint4 gv[CH], uv[CH], h[CH];
+  // every lane loads (chunk 0 past the row end, a valid address) and nothing
+  // is zeroed: the team's amax and stores leave those chunks out
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int64_t c = (int64_t)i * TEAM + tl;
-    gv[i] = ld16_if(gr, c, row_ok && c < nch);
-    uv[i] = ld16_if(gr + nch, c, row_ok && c < nch);
+    const int64_t cc = (row_ok && c < nch) ? c : 0;
+    gv[i] = ld16(gr + cc);
+    uv[i] = ld16(gr + nch + cc);
   }
 #pragma unroll
   for (int i = 0; i < CH; ++i) h[i] = silu_mul8(gv[i], uv[i]);   // silu(0) * 0 = +0
