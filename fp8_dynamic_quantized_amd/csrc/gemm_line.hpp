@@ -22,6 +22,9 @@ constexpr int GM = 8;  // tile rows per L2 group
 #ifndef FP8DQ_LINE_PERSIST
 #define FP8DQ_LINE_PERSIST 1
 #endif
+#ifndef FP8DQ_LINE_GF_AT
+#define FP8DQ_LINE_GF_AT 2   // block: odd-step MFMA slot where the next group's factor is formed
+#endif
 #ifndef FP8DQ_LINE_EARLY
 #define FP8DQ_LINE_EARLY 1
 #endif
@@ -70,16 +73,22 @@ constexpr int LBK = 128;                 // K bytes per pair (two MFMA steps)
 template <bool BLOCK, int BNP>
 struct LineCfg {
   static constexpr int BM = 256, BN = BNP;
-  static constexpr int NSL = BLOCK ? 3 : 2;                 // pair slots
+  // waves: 2 x 2; 256-wide block tiles take 2 x 4 (two waves per SIMD, each
+  // with the same 128 x 64 part as in a 256 x 128 tile)
+  static constexpr int NW = (BLOCK && BNP == 256) ? 8 : 4;
+  static constexpr int NSL = (BLOCK && BNP == 128) ? 3 : 2; // pair slots
   static constexpr int SLOT = (BM + BN) * LBK;
-  static constexpr int XQ = BM / 32, WQ = BN / 32;          // loads per wave per pair
+  static constexpr int XQ = BM / (8 * NW), WQ = BN / (8 * NW);  // loads per wave per pair
   static constexpr int NLD = XQ + WQ;
+  static constexpr int NBLK = BLOCK ? BN / 128 : 0;         // weight blocks across a tile
   static constexpr int SC = NSL * SLOT;                     // scale areas
   // per-channel: two tile-scale buffers [sx 256 | sw 256] (this tile's and
   // the next one's); block: the sx ring NSL x [256], then two buffers of a
-  // tile's weight-block scales sw [G], loaded in 64-entry chunks
+  // tile's weight-block scales [NBLK][G], loaded in 64-entry chunks
   static constexpr int SWB = SC + (BLOCK ? NSL * 1024 : 2 * 2048);
-  __host__ __device__ static int swsz(int K) { return BLOCK ? ((K / 128 + 63) / 64) * 256 : 0; }
+  __host__ __device__ static int swsz(int K) {
+    return BLOCK ? NBLK * ((K / 128 + 63) / 64) * 256 : 0;
+  }
   static size_t smem(int64_t K) { return (size_t)SWB + 2 * (size_t)swsz((int)K); }
 };
 
@@ -93,15 +102,16 @@ __device__ __forceinline__ uint32_t pk_bf16_rne(float lo, float hi) {
 }
 
 template <bool BLOCK, int BNP>
-__global__ __launch_bounds__(256, 1) void gemm_prefill_line_kernel(
+__global__ __launch_bounds__((64 * LineCfg<BLOCK, BNP>::NW), 1) void gemm_prefill_line_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint8_t* __restrict__ qw, const float* __restrict__ sw,
     uint16_t* __restrict__ y, int M, int N, int K, int tiles_m, int tiles_n) {
   using C = LineCfg<BLOCK, BNP>;
-  static_assert(BLOCK ? BNP == 128 : (BNP == 256 || BNP == 192), "tile widths built");
-  constexpr int BM = C::BM, BN = C::BN, NSL = C::NSL, SLOT = C::SLOT;
+  static_assert(BLOCK ? (BNP == 128 || BNP == 256) : (BNP == 256 || BNP == 192),
+                "tile widths built");
+  constexpr int BM = C::BM, BN = C::BN, NSL = C::NSL, SLOT = C::SLOT, NW = C::NW;
   constexpr int XQ = C::XQ, WQ = C::WQ, NLD = C::NLD;
-  constexpr int DTM = 128, DTN = BN / 2;
+  constexpr int DTM = 128, DTN = BN / (NW / 2);
   constexpr int DMJ = DTM / 32, DNI = DTN / 32;   // 32-row fragments per wave (m, n)
   constexpr int NM = DNI * DMJ;                   // MFMAs per step
   constexpr int NR = 2 * (DNI + DMJ);             // fragment halves per step
@@ -141,9 +151,9 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_line_kernel(
     n0 = (in_g / gm) * BN;
   };
 
-  // Loads: groups of 8 rows; wave w takes groups 4q + w. Lane l covers row
+  // Loads: groups of 8 rows; wave w takes groups NW q + w. Lane l covers row
   // 8g + l/8 and LDS chunk slot l%8, i.e. global chunk (l%8) ^ lswz(row)
-  // = (l%8) ^ (l/8) ^ w (independent of q).
+  // = (l%8) ^ (l/8) ^ (w%4) (independent of q).
   // operand offsets of the current tile
   uint32_t rowX[XQ], rowW[WQ];
   uint32_t sxoff = 0u;   // block: this wave's 64 rows of activation scales
@@ -154,17 +164,18 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_line_kernel(
     origin(v, m0, n0);
     const int ln = lane_now();
     const int r8 = 8 * wave + (ln >> 3);
-    const uint32_t cc = (uint32_t)(((ln & 7) ^ (ln >> 3) ^ wave) << 4);
+    const uint32_t cc = (uint32_t)(((ln & 7) ^ (ln >> 3) ^ (wave & 3)) << 4);
     // 24-bit multiplies (rows and K are below 2^24: K by the size rules,
     // rows because rows x K stays below 2^32 with K >= 256): 32-bit results,
     // where a full multiply-add would hold a 64-bit register pair
 #pragma unroll
     for (int q = 0; q < XQ; ++q)
-      rowX[q] = __umul24((uint32_t)min(m0 + 32 * q + r8, M - 1), (uint32_t)K) + cc;
+      rowX[q] = __umul24((uint32_t)min(m0 + 8 * NW * q + r8, M - 1), (uint32_t)K) + cc;
 #pragma unroll
     for (int q = 0; q < WQ; ++q)
-      rowW[q] = __umul24((uint32_t)min(n0 + 32 * q + r8, N - 1), (uint32_t)K) + cc;
-    sxoff = BLOCK ? (uint32_t)min(m0 + 64 * wave + ln, M - 1) * (uint32_t)G * 4u : 0u;
+      rowW[q] = __umul24((uint32_t)min(n0 + 8 * NW * q + r8, N - 1), (uint32_t)K) + cc;
+    // block: 64 rows of activation scales per wave (waves 4-7 repeat 0-3)
+    sxoff = BLOCK ? (uint32_t)min(m0 + 64 * (wave & 3) + ln, M - 1) * (uint32_t)G * 4u : 0u;
   };
   int v = blockIdx.x;
   set_tile(v);
@@ -174,11 +185,15 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_line_kernel(
   auto tile_scales = [&](int tm0, int tn0, int b) {
     const int lane = lane_now();
     if constexpr (BLOCK) {
-      // the tile's weight-block scales for every group (its 128 columns are one block)
-      const uint32_t swrow = (uint32_t)(tn0 / 128) * (uint32_t)G * 4u;
-      for (int c = wave; c * 64 < G; c += 4)
-        dma4(sw, swrow + (uint32_t)min(64 * c + lane, G - 1) * 4u,
+      // the scales of the tile's NBLK weight blocks for every group, in
+      // chunks of 64 groups (a block past N, in a ragged last tile, repeats
+      // the last one; its columns are not stored)
+      const int nch = (G + 63) / 64;
+      for (int c = wave; c < C::NBLK * nch; c += NW) {
+        const int blk = min(tn0 / 128 + c / nch, N / 128 - 1);
+        dma4(sw, (uint32_t)(blk * G + min(64 * (c % nch) + lane, G - 1)) * 4u,
              lds0 + C::SWB + (uint32_t)(b * SWSZ + 256 * c));
+      }
     } else {
       // 64 sx (rows) and 64 sw (columns) per wave
       const uint32_t sb = lds0 + C::SC + (uint32_t)(b * 2048);
@@ -193,10 +208,10 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_line_kernel(
     if (u < NLD) {
       const size_t koff = (size_t)pc * LBK;
       const uint32_t sb = lds0 + (uint32_t)(si * SLOT);
-      if (u < XQ) dma16(qx + koff, rowX[u], sb + (uint32_t)((4 * u + wave) * 1024));
-      else dma16(qw + koff, rowW[u - XQ], sb + XB + (uint32_t)((4 * (u - XQ) + wave) * 1024));
+      if (u < XQ) dma16(qx + koff, rowX[u], sb + (uint32_t)((NW * u + wave) * 1024));
+      else dma16(qw + koff, rowW[u - XQ], sb + XB + (uint32_t)((NW * (u - XQ) + wave) * 1024));
     } else if (BLOCK && u == NLD) {
-      dma4(sx, sxoff + (uint32_t)pc * 4u, lds0 + C::SC + (uint32_t)(si * 1024 + 256 * wave));
+      dma4(sx, sxoff + (uint32_t)pc * 4u, lds0 + C::SC + (uint32_t)(si * 1024 + 256 * (wave & 3)));
     }
   };
   // a tile's scales and pairs 0 .. NSL-1 into slots s0, s0+1, ...
@@ -247,13 +262,23 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_line_kernel(
   float fcur[DMJ], fnext[DMJ], rho[DMJ];
 #pragma unroll
   for (int j = 0; j < DMJ; ++j) { fcur[j] = 0.f; fnext[j] = 0.f; rho[j] = 1.f; }
-  auto group_factor = [&](int g, int si) {   // f_g of this lane's rows -> rho, fnext
+  // group g's scales of this lane's rows, read from LDS (gsx, gsw) ...
+  float gsx[DMJ], gsw = 0.f;
+  auto group_scales = [&](int g, int si) {
     const int lr = lane_now() & 31;
     const float* sxs = reinterpret_cast<const float*>(smem + C::SC + si * 1024);
-    const float swg = reinterpret_cast<const float*>(smem + C::SWB + par * SWSZ)[min(g, G - 1)];
+    // this wave's 64 columns lie in weight block (wn * DTN) / 128 of the tile
+    const int blk = (wn * DTN) / 128;
+    gsw = reinterpret_cast<const float*>(smem + C::SWB + par * SWSZ)[blk * ((G + 63) / 64) * 64 +
+                                                                     min(g, G - 1)];
+#pragma unroll
+    for (int j = 0; j < DMJ; ++j) gsx[j] = sxs[wm * DTM + 32 * j + lr];
+  };
+  // ... and f_g -> rho, fnext (formed later, so the reads' latency is hidden)
+  auto group_factor = [&]() {
 #pragma unroll
     for (int j = 0; j < DMJ; ++j) {
-      const float f = sxs[wm * DTM + 32 * j + lr] * swg;
+      const float f = gsx[j] * gsw;
       const bool live = f != 0.0f;
       rho[j] = live ? fcur[j] * __builtin_amdgcn_rcpf(f) : 1.0f;
       fnext[j] = live ? f : fcur[j];
@@ -286,7 +311,8 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_line_kernel(
     if constexpr (BLOCK) {
 #pragma unroll
       for (int j = 0; j < DMJ; ++j) { fcur[j] = 0.f; rho[j] = 1.f; }
-      group_factor(0, cs);
+      group_scales(0, cs);
+      group_factor();
 #pragma unroll
       for (int j = 0; j < DMJ; ++j) fcur[j] = fnext[j];   // rho of group 0 is unused
     }
@@ -327,7 +353,10 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_line_kernel(
       // wave's reads of the slot refilled below are done
       __builtin_amdgcn_s_waitcnt(vmcnt_imm((NSL - 2) * (NLD + NSC)) & ~0x0F00);
       asm volatile("s_barrier" ::: "memory");
-      if constexpr (BLOCK) group_factor(kt / 2 + 1, ns);
+      if constexpr (BLOCK) {
+        group_scales(kt / 2 + 1, ns);
+        if (FP8DQ_LINE_GF_AT < 0) group_factor();
+      }
     }
     const int rs = cur == 0 ? cs : ns;
     Offs oA, oB;
@@ -378,6 +407,9 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_line_kernel(
             if (w < NLD + NSC) issue(cs, kt / 2 + NSL, w);
           }
         }
+      }
+      if constexpr (BLOCK && cur == 1 && FP8DQ_LINE_GF_AT >= 0) {
+        if (more && t == FP8DQ_LINE_GF_AT) group_factor();
       }
       const int i = t / DMJ, j = t % DMJ;
       if constexpr (first) {
@@ -520,7 +552,7 @@ void launch_line(const uint8_t* qx, const float* sx, const uint8_t* qw, const fl
     if (ncu > 0 && ncu % 8 == 0 && ntiles > ncu) grid = ncu;
   }
 #endif
-  hipLaunchKernelGGL((gemm_prefill_line_kernel<BLOCK, BNP>), dim3((unsigned)grid), dim3(256),
+  hipLaunchKernelGGL((gemm_prefill_line_kernel<BLOCK, BNP>), dim3((unsigned)grid), dim3(64 * C::NW),
                      C::smem(K), st, qx, sx, qw, sw, (uint16_t*)y, (int)M, (int)N, (int)K,
                      tiles_m, tiles_n);
 }

@@ -215,11 +215,14 @@ def test_gemm_wide_tiles_ragged(F, M, N, K):
     assert_y_close(host_bf16_f64(y), O.linear_per_channel(qx, sx, qw, sw), "y")
 
 
-@pytest.mark.parametrize("M,N,K", [(4352, 4096, 384), (4200, 2176, 1152), (2100, 4352, 512)])
+@pytest.mark.parametrize("M,N,K", [(4352, 4096, 384), (4200, 2176, 1152), (2100, 4352, 512),
+                                   (8192, 4096, 640)])
 def test_gemm_block_wide_tiles(F, M, N, K):
-    """Block-scaled GEMM with more tiles than CUs (workgroups walk several
-    tiles), ragged M, the shortest K of that mode (three groups), and
-    group scales that differ by orders of magnitude between groups."""
+    """Block-scaled GEMM with more tiles than CUs, ragged M, the shortest K
+    of that mode (three groups), and group scales that differ by orders of
+    magnitude between groups. On 256 CUs the first shape runs 256 x 128
+    tiles; the others 256 x 256 tiles (8 waves), one of them with a last
+    tile column half past N (N = 2176) and one with two full rounds."""
     say(f"gemm block wide {M}x{N}x{K}")
     G = K // 128
     rng = np.random.default_rng(M + 3 * N + K)
