@@ -33,8 +33,9 @@ constexpr int GM = 8;  // tile rows per L2 group
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 // ---------------------------------------------------------------------------
-// Whole-line kernels: 256 x BN tiles (BN = 256 or 192 per-channel, 128 block),
-// v_mfma_f32_32x32x64_f8f6f4, 4 waves (2 x 2).
+// Whole-line kernels: 256 x BN tiles (BN = 256 or 192 per-channel, 128 or 256
+// block), v_mfma_f32_32x32x64_f8f6f4, 4 waves (2 x 2); 256 x 256 block tiles
+// take 8 waves (2 x 4, two per SIMD), each with a 128 x 64 part.
 //  * A load instruction moves 8 rows x 128 bytes (two 64-byte MFMA K steps of
 //    each row): every request is a whole 128-byte line. The L2 -> LDS path
 //    costs the same per line touched, so 64-byte row pieces (16 rows per
@@ -52,12 +53,16 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 //    read the second half of a pair that has already landed.
 //  * Per-channel: NSL = 2 (two 64 KB slots), the tile's sx / sw in LDS.
 //  * Block (128 x 128 weight blocks, 128-wide activation groups): NSL = 3
-//    (48 KB slots); a pair is exactly one scale group g, whose 256 activation
+//    48 KB slots for 256 x 128 tiles, 2 x 64 KB for 256 x 256 ones; a pair
+//    is exactly one scale group g, whose 256 activation
 //    scales ride with the pair into a per-slot LDS ring, and the tile's
 //    weight-block scales for every g are loaded once. One accumulator carries
 //    the sum in units of the current factor f_g = sx[m,g] * sw[nb,g]: it is
 //    multiplied by f_{g-1} / f_g before group g's first MFMAs (a zero factor,
 //    an all-zero group, leaves it alone) and by the last factor at the end.
+//    The next group's scales are read right after the odd step's barrier and
+//    its factor is formed a few MFMAs later, so the matrix core does not
+//    wait for those reads.
 //  * Epilogue from registers: scale, round to bf16, and pair lanes l and l+32
 //    with v_permlane32_swap so each lane stores 16 contiguous bytes.
 //  * A workgroup may walk several tiles (blockIdx.x, + gridDim.x, ...): after
@@ -538,16 +543,17 @@ void launch_line(const uint8_t* qx, const float* sx, const uint8_t* qw, const fl
   const int tiles_m = (int)((M + C::BM - 1) / C::BM);
   const int tiles_n = (int)((N + C::BN - 1) / C::BN);
   const int ntiles = tiles_m * tiles_n;
-  // Per-channel: persistent when there are more tiles than CUs (one
-  // workgroup per CU walks its tiles; the next tile's scales and first pairs
-  // load under the current one's epilogue). Measured 1.5-3.5 % faster on
-  // the 8B and long-context gate_up shapes. The block kernel (twice the
-  // tiles, 16 per CU on the 3B gate_up) keeps one tile per workgroup: there
-  // the dispatcher's dynamic assignment balances the CUs better than a
-  // fixed one did (6 % slower persistent).
+  // Persistent when there are more tiles than CUs (one workgroup per CU
+  // walks its tiles; the next tile's scales and first pairs load under the
+  // current one's epilogue): per-channel measured 1.5-3.5 % faster on the 8B
+  // and long-context gate_up shapes, block 256 x 256 tiles 1-5 % faster on
+  // the 3B qkv and gate_up shapes. 256 x 128 block tiles (16 per CU on the
+  // 3B gate_up) keep one tile per workgroup: there the dispatcher's dynamic
+  // assignment balanced the CUs better than a fixed one (6 % slower
+  // persistent).
   int grid = ntiles;
 #if FP8DQ_LINE_PERSIST
-  if (!BLOCK) {
+  if (!BLOCK || BNP == 256) {
     const int ncu = cu_count();
     if (ncu > 0 && ncu % 8 == 0 && ntiles > ncu) grid = ncu;
   }
