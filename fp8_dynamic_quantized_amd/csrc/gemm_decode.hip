@@ -56,6 +56,19 @@ __device__ __forceinline__ v8i gload_frag(const uint8_t* p) {
   return r;
 }
 
+// Token-row fragment through a bounds-checked buffer load: a lane whose
+// offset lies past the buffer's size reads zeros without a memory access.
+// (Raw buffer resource, word 3 = 0x00020000 on gfx9-family parts.)
+__device__ __forceinline__ v8i bload_frag(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16u), 0, 0);
+  v8i res;
+  res[0] = (int)lo.x; res[1] = (int)lo.y; res[2] = (int)lo.z; res[3] = (int)lo.w;
+  res[4] = (int)hi.x; res[5] = (int)hi.y; res[6] = (int)hi.z; res[7] = (int)hi.w;
+  return res;
+}
+
 template <int MB, int NB, int D, bool BLOCK>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx,
@@ -73,15 +86,22 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
   const int kt1 = min(KT, kt0 + kt_per_split);
 
   const uint8_t* wp[NB];
-  const uint8_t* xp[MB];
   int xrow[MB];
+  // Token rows: lanes of MFMA padding rows (16 j + lr >= M) get an offset past
+  // the buffer and load nothing. Their outputs are dropped; loads repeating a
+  // real row cost the load path as much as distinct ones (at M = 1, 15 of 16
+  // token rows are padding). M * K < 2^30 on this path (M <= 64, K < 2^24).
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)qx, (short)0, M * K, 0x00020000);
+  uint32_t xoff[MB];
 #pragma unroll
   for (int i = 0; i < NB; ++i)
     wp[i] = qw + (int64_t)min(n0 + 16 * i + lr, N - 1) * K + kg * 32;
 #pragma unroll
   for (int j = 0; j < MB; ++j) {
     xrow[j] = min(16 * j + lr, M - 1);
-    xp[j] = qx + (int64_t)xrow[j] * K + kg * 32;
+    xoff[j] = 16 * j + lr < M ? (uint32_t)(16 * j + lr) * (uint32_t)K + (uint32_t)(kg * 32)
+                              : 0x80000000u;
   }
 
   v4f acc[NB][MB];
@@ -95,46 +115,64 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
   const int cnt = first < kt1 ? (kt1 - first + 3) / 4 : 0;
 
   v8i a[D][NB], b[D][MB];
+  float sxr[D][MB], swr[D][NB];   // block: the step's group scales, loaded with it
+  // (a step index past the row's end is clamped: the prologue loads D steps
+  // without conditions, so the loop starts with a known number in flight)
   auto load = [&](int d, int t) {
-    const int64_t k0 = (int64_t)(first + 4 * t) * BK;
+    const int kt = min(first + 4 * t, KT - 1);
+    const int64_t k0 = (int64_t)kt * BK;
 #pragma unroll
     for (int i = 0; i < NB; ++i)
       a[d][i] = FP8DQ_DEC_NT ? gload_frag_nt(wp[i] + k0) : gload_frag(wp[i] + k0);
 #pragma unroll
-    for (int j = 0; j < MB; ++j) b[d][j] = gload_frag(xp[j] + k0);
+    for (int j = 0; j < MB; ++j) b[d][j] = bload_frag(xrs, xoff[j] + (uint32_t)k0);
+    if (BLOCK) {
+      const int g = kt;
+#pragma unroll
+      for (int j = 0; j < MB; ++j) sxr[d][j] = sx[(int64_t)xrow[j] * G + g];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) swr[d][i] = sw[(int64_t)((n0 + 16 * i) >> 7) * G + g];
+    }
+  };
+  auto compute = [&](int d) {
+    if (BLOCK) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < MB; ++j) {
+          const v4f p = mfma_e4m3_16x16x128(a[d][i], b[d][j], v4f{0.f, 0.f, 0.f, 0.f});
+          const float sc = sxr[d][j] * swr[d][i];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], sc, acc[i][j][r]);
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+          acc[i][j] = mfma_e4m3_16x16x128(a[d][i], b[d][j], acc[i][j]);
+    }
   };
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (d < cnt) load(d, d);
-
-  for (int t0 = 0; t0 < cnt; t0 += D) {
+  for (int d = 0; d < D; ++d) load(d, d);
+  // Steady state: every step of a batch has a step D ahead to load, so the
+  // body has no conditions and each step waits only for its own loads (the
+  // compiler cannot count loads across the tail's conditions and waits for
+  // all of them there, draining the D steps in flight).
+  int t0 = 0;
+  for (; t0 + 2 * D <= cnt; t0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      compute(d);
+      load(d, t0 + d + D);
+    }
+  }
+  for (; t0 < cnt; t0 += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int t = t0 + d;
       if (t < cnt) {
-        if (BLOCK) {
-          const int g = first + 4 * t;
-          float sxg[MB];
-#pragma unroll
-          for (int j = 0; j < MB; ++j) sxg[j] = sx[(int64_t)xrow[j] * G + g];
-#pragma unroll
-          for (int i = 0; i < NB; ++i) {
-            const float swg = sw[(int64_t)((n0 + 16 * i) >> 7) * G + g];
-#pragma unroll
-            for (int j = 0; j < MB; ++j) {
-              const v4f p = mfma_e4m3_16x16x128(a[d][i], b[d][j], v4f{0.f, 0.f, 0.f, 0.f});
-              const float sc = sxg[j] * swg;
-#pragma unroll
-              for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], sc, acc[i][j][r]);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < NB; ++i)
-#pragma unroll
-            for (int j = 0; j < MB; ++j)
-              acc[i][j] = mfma_e4m3_16x16x128(a[d][i], b[d][j], acc[i][j]);
-        }
+        compute(d);
         if (t + D < cnt) load(d, t + D);
       }
     }
