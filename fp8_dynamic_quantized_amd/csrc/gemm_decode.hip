@@ -540,9 +540,15 @@ DecodePlan plan_decode(int64_t M, int64_t N, int64_t K) {
   if (p.line) {
     // Whole-line kernel: 128 weight rows per workgroup, two workgroups per
     // CU. Split K until there are >= 384 workgroups (1.5 per CU), keeping at
-    // least 8 K steps per slice.
+    // least 8 K steps per slice. Long rows with fewer row blocks than CUs
+    // split to 512 workgroups (two on every CU): there the slices' fp32
+    // partials are small next to the weights. Measured on the 70B down
+    // (K = 28672) at 32 and 64 tokens: 8 slices 59.4 / 63.9 us against 6
+    // slices 63.7 / 68.3 us; on K = 8192 shapes 512 workgroups were no faster
+    // (o) or slower (qkv, gate_up).
     const int64_t wg0 = (N + DL_BN - 1) / DL_BN;
-    int64_t s = (384 + wg0 - 1) / wg0;
+    const int64_t target = (K >= 16384 && wg0 < 256) ? 512 : 384;
+    int64_t s = (target + wg0 - 1) / wg0;
     if (s > KT / 8) s = KT / 8;
     if (s < 1) s = 1;
     p.kt_per_split = (int)((KT + s - 1) / s);

@@ -423,7 +423,9 @@ DECODE_CASES = [(1, 8192, 8192), (5, 100, 1664), (16, 1024, 4096), (17, 520, 320
                 # split-K with one row, ragged N, 16 rows, the shortest K, the
                 # longest K at one row
                 (1, 64, 8192), (3, 100, 2048), (16, 200, 1920), (4, 32, 128),
-                (1, 8192, 28672)]
+                (1, 8192, 28672),
+                # whole-line kernel on long rows (8 and 16 K slices)
+                (64, 8192, 28672), (40, 3000, 16384)]
 
 
 @pytest.mark.parametrize("M,N,K", DECODE_CASES)
