@@ -237,7 +237,11 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
 }
 
 // y[m,n] = bf16( (sum over splits, in order, of ws[s,m,n]) * scales )
-template <bool BLOCK>
+// S > 0: the number of slices is a compile-time constant, so all S partials
+// of an output are loaded before the first add (one memory latency instead of
+// S); S = 0: any number, one partial at a time. Either way the partials are
+// added in slice order.
+template <bool BLOCK, int S>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(
     const float* __restrict__ ws, const float* __restrict__ sx,
     const float* __restrict__ sw, uint16_t* __restrict__ y, int M, int N,
@@ -246,10 +250,35 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
   const int64_t total = (int64_t)M * N;
   if (idx >= total) return;
   const int64_t m = idx / N, n = idx % N;
-  float s = ws[idx];
-  for (int k = 1; k < splits; ++k) s += ws[(int64_t)k * total + idx];
+  float s;
+  if constexpr (S > 0) {
+    float p[S];
+#pragma unroll
+    for (int k = 0; k < S; ++k) p[k] = ws[(int64_t)k * total + idx];
+    s = p[0];
+#pragma unroll
+    for (int k = 1; k < S; ++k) s += p[k];
+  } else {
+    s = ws[idx];
+    for (int k = 1; k < splits; ++k) s += ws[(int64_t)k * total + idx];
+  }
   const float v = BLOCK ? s : s * sx[m] * sw[n];
   y[idx] = (uint16_t)f32_to_bf16_rne(v);
+}
+
+template <bool BLOCK, int S = 2>
+void launch_reduce(const float* ws, const float* sx, const float* sw, uint16_t* y,
+                   int64_t M, int64_t N, int splits, hipStream_t st) {
+  if constexpr (S <= 16) {
+    if (splits != S) {
+      launch_reduce<BLOCK, S + 1>(ws, sx, sw, y, M, N, splits, st);
+      return;
+    }
+  }
+  constexpr int SK = S <= 16 ? S : 0;
+  const int64_t total = M * N;
+  hipLaunchKernelGGL((splitk_reduce_kernel<BLOCK, SK>), dim3((unsigned)((total + 255) / 256)),
+                     dim3(256), 0, st, ws, sx, sw, y, (int)M, (int)N, splits);
 }
 
 // ---------------------------------------------------------------------------
@@ -467,12 +496,7 @@ void launch_line_dec(const uint8_t* qx, const float* sx, const uint8_t* qw,
   hipLaunchKernelGGL((gemm_decode_line_kernel<MB, BLOCK>), dim3(gx, (unsigned)p.splits),
                      dim3(256), smem, st, qx, sx, qw, sw, (uint16_t*)y, part, (int)M, (int)N,
                      (int)K, p.kt_per_split);
-  if (p.splits > 1) {
-    const int64_t total = M * N;
-    hipLaunchKernelGGL((splitk_reduce_kernel<BLOCK>),
-                       dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                       ws, sx, sw, (uint16_t*)y, (int)M, (int)N, p.splits);
-  }
+  if (p.splits > 1) launch_reduce<BLOCK>(ws, sx, sw, (uint16_t*)y, M, N, p.splits, st);
 }
 
 template <int MB, int NB, int D, bool BLOCK>
@@ -485,12 +509,7 @@ void launch_cfg(const uint8_t* qx, const float* sx, const uint8_t* qw,
                      dim3(gx, (unsigned)p.splits), dim3(256), 0, st, qx, sx, qw,
                      sw, (uint16_t*)y, part, (int)M, (int)N, (int)K,
                      p.kt_per_split);
-  if (p.splits > 1) {
-    const int64_t total = M * N;
-    hipLaunchKernelGGL((splitk_reduce_kernel<BLOCK>),
-                       dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                       ws, sx, sw, (uint16_t*)y, (int)M, (int)N, p.splits);
-  }
+  if (p.splits > 1) launch_reduce<BLOCK>(ws, sx, sw, (uint16_t*)y, M, N, p.splits, st);
 }
 
 template <int MB, bool BLOCK>

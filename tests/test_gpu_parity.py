@@ -424,8 +424,9 @@ DECODE_CASES = [(1, 8192, 8192), (5, 100, 1664), (16, 1024, 4096), (17, 520, 320
                 # longest K at one row
                 (1, 64, 8192), (3, 100, 2048), (16, 200, 1920), (4, 32, 128),
                 (1, 8192, 28672),
-                # whole-line kernel on long rows (8 and 16 K slices)
-                (64, 8192, 28672), (40, 3000, 16384)]
+                # whole-line kernel on long rows (8, 16 and 20 K slices; more
+                # than 16 slices take the reduction's general loop)
+                (64, 8192, 28672), (40, 3000, 16384), (20, 100, 20480)]
 
 
 @pytest.mark.parametrize("M,N,K", DECODE_CASES)
