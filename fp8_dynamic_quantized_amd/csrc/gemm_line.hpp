@@ -3,7 +3,8 @@
 // (gemm_block.hip, built with the MFMA accumulators in ordinary VGPRs so the
 // per-group rescale is a plain multiply).
 //
-// What is computed: Y[m,n] = bf16( sum_k val(qx[m,k]) val(qw[n,k]) * scales ),
+// What is computed: Y[m,n] = bf16( sum_k val(qx[m,k]) val(qw[n,k]) * scales )
+// (Y's rows ldy elements apart),
 // per-token x per-channel scales (Llama-3.1-8B-Instruct-FP8-Dynamic page, FP8
 // dynamic quantization table) or 128-wide activation groups x 128 x 128
 // weight blocks (Llama-3.2-3B-Instruct-FP8-Block page, FP8 block
@@ -110,7 +111,7 @@ template <bool BLOCK, int BNP>
 __global__ __launch_bounds__((64 * LineCfg<BLOCK, BNP>::NW), 1) void gemm_prefill_line_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint8_t* __restrict__ qw, const float* __restrict__ sw,
-    uint16_t* __restrict__ y, int M, int N, int K, int tiles_m, int tiles_n) {
+    uint16_t* __restrict__ y, int M, int N, int K, int ldy, int tiles_m, int tiles_n) {
   using C = LineCfg<BLOCK, BNP>;
   static_assert(BLOCK ? (BNP == 128 || BNP == 256) : (BNP == 256 || BNP == 192),
                 "tile widths built");
@@ -439,7 +440,7 @@ __global__ __launch_bounds__((64 * LineCfg<BLOCK, BNP>::NW), 1) void gemm_prefil
   using T = std::true_type;
   using F = std::false_type;
   const int KT = K / 64;   // even, >= 4
-  const bool vec = (N & 7) == 0;
+  const bool vec = ((N | ldy) & 7) == 0;
 
   for (;;) {
     step(0, I0(), T(), T());
@@ -503,7 +504,7 @@ __global__ __launch_bounds__((64 * LineCfg<BLOCK, BNP>::NW), 1) void gemm_prefil
           const uint4 o = make_uint4(s0[0], s1[0], s0[1], s1[1]);
           const int n = en0 + wn * DTN + 32 * i + 16 * qp + 8 * ekh;
           if (m < M) {
-            uint16_t* out = y + (int64_t)m * N + n;
+            uint16_t* out = y + (int64_t)m * ldy + n;
             if (vec && n + 7 < N) {
               *reinterpret_cast<uint4*>(out) = o;
             } else {
@@ -531,10 +532,12 @@ inline int cu_count() {
   return ncu;
 }
 
+// y: rows of ldy elements (0: N), of which the first N are written.
 template <bool BLOCK, int BNP>
 void launch_line(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
-                 void* y, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+                 void* y, int64_t M, int64_t N, int64_t K, hipStream_t st, int64_t ldy = 0) {
   using C = LineCfg<BLOCK, BNP>;
+  if (ldy == 0) ldy = N;
   static std::once_flag once;
   std::call_once(once, [] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_prefill_line_kernel<BLOCK, BNP>),
@@ -560,7 +563,7 @@ void launch_line(const uint8_t* qx, const float* sx, const uint8_t* qw, const fl
 #endif
   hipLaunchKernelGGL((gemm_prefill_line_kernel<BLOCK, BNP>), dim3((unsigned)grid), dim3(64 * C::NW),
                      C::smem(K), st, qx, sx, qw, sw, (uint16_t*)y, (int)M, (int)N, (int)K,
-                     tiles_m, tiles_n);
+                     (int)ldy, tiles_m, tiles_n);
 }
 
 }  // namespace

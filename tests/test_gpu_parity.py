@@ -216,14 +216,19 @@ def test_gemm_wide_tiles_ragged(F, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(4352, 4096, 384), (4200, 2176, 1152), (2100, 4352, 512),
-                                   (8192, 4096, 640), (6300, 4224, 384)])
+                                   (8192, 4096, 640), (6300, 4224, 384), (8192, 5120, 384)])
 def test_gemm_block_wide_tiles(F, M, N, K):
     """Block-scaled GEMM with more tiles than CUs, ragged M, the shortest K
     of that mode (three groups), and group scales that differ by orders of
-    magnitude between groups. On 256 CUs the first shape runs 256 x 128
-    tiles; the others 256 x 256 tiles (8 waves), with a last tile column
-    half past N (N = 2176, 4224). The last two have more of those tiles than
-    CUs, so workgroups walk two tiles each (all of them, or 169 of 256)."""
+    magnitude between groups. On 256 CUs:
+    - the first shape runs its first 2304 columns as 256 x 256 tiles and the
+      rest as 256 x 128 tiles, in two launches;
+    - the next four run 256 x 256 tiles only (8 waves). Two of them have a
+      last tile column half past N (N = 2176, 4224). Two have more such
+      tiles than CUs, so workgroups walk two tiles each (all of them, or 169
+      of 256);
+    - the last runs two rounds of 256 x 256 tiles (4096 columns), then one
+      of 256 x 128."""
     say(f"gemm block wide {M}x{N}x{K}")
     G = K // 128
     rng = np.random.default_rng(M + 3 * N + K)
