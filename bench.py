@@ -382,6 +382,76 @@ def bench_block(F, torch):
     return out
 
 
+def bench_long_small(F, torch):
+    """c5: the Llama-3.1-8B gate_up at M = 32768 tokens of Student-t(3)
+    activations with zero rows and planted values past 448 (MFMA-bound);
+    c1: one 4096 -> 1024 linear at M = 16 tokens (weight streaming, launch-
+    latency-bound). Both are fp8_linear end to end (quantize + GEMM), also
+    split into its two launches for c5. Medians of batches of back-to-back
+    launches, HIP events."""
+    import synth
+    out = {}
+    d = synth.workload(5, 0)
+    M, K, N = d["M"], d["K"], d["N"]
+    log(f"long-context setup: gate_up {K}->{N}, M={M} (Student-t, "
+        f"{len(d['zero_rows'])} zero rows, {len(d['planted'])} planted values)")
+    x = to_dev(d["x"], torch)
+    w = to_dev(d["w"], torch)
+    del d
+    qw, sw = F.fp8_quant_act(w)
+    del w
+    qx = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sx = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    l_us = _time_us(torch, lambda: F.fp8_linear(x, qw, sw, y=y, qx_out=qx, sx_out=sx),
+                    reps=5, warm=2, batches=5)
+    q_us = _time_us(torch, lambda: F.fp8_quant_act(x, q=qx, scale=sx), reps=10, warm=2, batches=5)
+    g_us = _time_us(torch, lambda: F.fp8_gemm(qx, sx, qw, sw, y=y), reps=5, warm=2, batches=5)
+    fl = 2 * M * N * K
+    out["c5_gate_up"] = {
+        "linear_us": round(l_us, 1), "linear_tflops": round(fl / (l_us * 1e-6) / 1e12, 1),
+        "frac": round(fl / (l_us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
+        "gemm_us": round(g_us, 1), "gemm_tflops": round(fl / (g_us * 1e-6) / 1e12, 1),
+        "quant_us": round(q_us, 2), "quant_gbs": round((3 * M * K + 4 * M) / (q_us * 1e-6) / 1e9, 1),
+        "shape": f"[{M},{K}] Student-t(3) x [{N},{K}] -> bf16 [{M},{N}]"}
+    log(f"  c5 gate_up: linear {l_us:.0f} us ({fl / (l_us * 1e-6) / 1e12:.0f} TFLOP/s), "
+        f"GEMM {g_us:.0f} us, quant {q_us:.1f} us")
+    del x, qx, sx, y, qw, sw
+    torch.cuda.empty_cache()
+
+    d = synth.workload(1, 0)
+    M, K, N = d["M"], d["K"], d["N"]
+    log(f"small setup: {K}->{N}, M={M}")
+    x = to_dev(d["x"], torch)
+    # cold weights: rotate distinct quantized copies, >= 2 GB in all
+    copies = max(2, (2 << 30) // (N * K) + 1)
+    w = to_dev(d["w"], torch)
+    qw0, sw = F.fp8_quant_act(w)
+    del w
+    qws = [qw0.clone() for _ in range(copies)]
+    del qw0
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    qx = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sx = torch.empty((M,), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(16, F.fp8_workspace_bytes(M, N, K)), dtype=torch.uint8, device="cuda")
+    it = [0]
+
+    def run():
+        F.fp8_linear(x, qws[it[0] % copies], sw, y=y, qx_out=qx, sx_out=sx, ws=ws)
+        it[0] += 1
+    us = _time_us(torch, run, reps=20, warm=5, batches=7)
+    wbytes = N * K + 4 * N
+    out["c1_single"] = {"linear_us": round(us, 2),
+                        "weight_gbs": round(wbytes / (us * 1e-6) / 1e9, 1),
+                        "frac": round(wbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                        "shape": f"[{M},{K}] x [{N},{K}] -> bf16 [{M},{N}], "
+                                 f"{copies} weight copies rotated"}
+    log(f"  c1: linear {us:.1f} us, weight {wbytes / (us * 1e-6) / 1e9:.0f} GB/s")
+    del x, qws, y, qx, sx, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration(torch):
     src = torch.randint(0, 255, (COPY_BYTES,), dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -438,6 +508,8 @@ def main():
                     help="skip the block-variant section (Llama-3.2-3B shapes)")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the fused-producer / calibration / KV-cache section")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long-context (M = 32768) and 16-token sections")
     ap.add_argument("--linears", default="qkv,o,gate_up,down",
                     help="prefill linears to run (profiling runs that must tell "
                          "the gate_up launches apart: every per-channel linear "
@@ -514,6 +586,8 @@ def main():
         out["decode"] = bench_decode(F, torch)
     if not args.no_block:
         out["block"] = bench_block(F, torch)
+    if not args.no_long:
+        out["long_small"] = bench_long_small(F, torch)
     if not args.no_next:
         log("fused producers, calibration, KV cache ...")
         out["next_rows"] = bench_next_rows(F, torch)

@@ -425,10 +425,12 @@ def test_c5_full_size_sampled(F):
 DECODE_CASES = [(1, 8192, 8192), (5, 100, 1664), (16, 1024, 4096), (17, 520, 3200),
                 (33, 4096, 896), (64, 10240, 8192), (64, 33, 128), (2, 2048, 28672),
                 (8, 57344, 8192), (48, 1000, 1152), (50, 130, 256),
-                # split-K with one row, ragged N, 16 rows, the shortest K, the
-                # longest K at one row
+                # few weight rows at one token, ragged N, 16 tokens, the
+                # shortest K (unsplit: K < 16384), the longest K at one token
                 (1, 64, 8192), (3, 100, 2048), (16, 200, 1920), (4, 32, 128),
                 (1, 8192, 28672),
+                # register kernel split on a long row at one token
+                (1, 64, 16384),
                 # whole-line kernel on long rows (8, 16 and 20 K slices; more
                 # than 16 slices take the reduction's general loop)
                 (64, 8192, 28672), (40, 3000, 16384), (20, 100, 20480)]
