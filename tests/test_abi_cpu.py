@@ -88,17 +88,19 @@ def test_gemm_block_needs_n_multiple_of_128(L):
 
 
 def test_workspace_rules(L):
-    # a small-N decode shape splits K and needs a workspace; prefill needs none
-    need = F.fp8_workspace_bytes(16, 1024, 4096)
+    # a small-N decode shape with long rows splits K and needs a workspace;
+    # with short rows (K < 16384) it runs unsplit; prefill needs none
+    need = F.fp8_workspace_bytes(16, 1024, 16384)
     assert need > 0 and need % 4 == 0
+    assert F.fp8_workspace_bytes(16, 1024, 4096) == 0
     assert F.fp8_workspace_bytes(4096, 4096, 4096) == 0
-    assert F.fp8_workspace_bytes(16, 1024, 4096, flags=F.FORCE_PREFILL) == 0
+    assert F.fp8_workspace_bytes(16, 1024, 16384, flags=F.FORCE_PREFILL) == 0
     assert F.fp8_workspace_bytes(16, 1024, 100) == 0       # invalid K -> 0
     assert F.fp8_workspace_bytes(16, 1000, 4096, block=True) == 0  # invalid N
     g = L.fp8_gemm
-    assert g(A, A, A, A, A, 16, 1024, 4096, 0, None, 0, None) == -1
-    assert g(A, A, A, A, A, 16, 1024, 4096, 0, A, need - 4, None) == -4
-    assert g(A, A, A, A, A, 16, 1024, 4096, 0, MIS, need, None) == -3
+    assert g(A, A, A, A, A, 16, 1024, 16384, 0, None, 0, None) == -1
+    assert g(A, A, A, A, A, 16, 1024, 16384, 0, A, need - 4, None) == -4
+    assert g(A, A, A, A, A, 16, 1024, 16384, 0, MIS, need, None) == -3
     # M beyond one decode slab uses the slab's workspace size
     assert F.fp8_workspace_bytes(200, 1024, 4096, flags=F.FORCE_DECODE) == \
         F.fp8_workspace_bytes(64, 1024, 4096)
