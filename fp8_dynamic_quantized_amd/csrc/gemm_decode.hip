@@ -17,9 +17,10 @@
 //  * MFMA operand A = 16 weight rows, B = 16 token rows (M padded by
 //    clamping the row index; the padded outputs are dropped);
 //  * the 4 waves' partial sums are added in a fixed order through LDS;
-//  * when N alone gives too few workgroups, K is also split across the grid
-//    (grid.y): fp32 partials go to a workspace and a second kernel adds them
-//    in split order and applies the epilogue -- deterministic.
+//  * when N alone gives too few workgroups and the rows are long (K >=
+//    16384), K is also split across the grid (grid.y): fp32 partials go to a
+//    workspace and a second kernel adds them in split order and applies the
+//    epilogue -- deterministic.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
