@@ -14,8 +14,9 @@
 //  * each wave keeps D K-steps of fragments in flight (loads for step t+D
 //    issue right after step t's MFMAs); weight loads are plain loads
 //    (non-temporal hints measured slower);
-//  * MFMA operand A = 16 weight rows, B = 16 token rows (M padded by
-//    clamping the row index; the padded outputs are dropped);
+//  * MFMA operand A = 16 weight rows, B = 16 token rows (rows past M read
+//    zeros through a bounds-checked load, with no memory access; their
+//    outputs are dropped);
 //  * the 4 waves' partial sums are added in a fixed order through LDS;
 //  * when N alone gives too few workgroups and the rows are long (K >=
 //    16384), K is also split across the grid (grid.y): fp32 partials go to a
