@@ -23,9 +23,13 @@ namespace {
 // X blocks in the XCD's 4 MB L2 while its W blocks stream through; measured
 // against 8 rows, alternating builds on one box: per-channel with 4 rows, 8B
 // o +6 %, down +3 %, gate_up +2 %; block with 2 rows, 3B gate_up +30 %
-// (4 rows: +19 %), the other shapes within 1-3 %.
+// (4 rows: +19 %; 1 row: +25 %), the other shapes within 1-3 %. With 64 or
+// more tile rows (M >= 16384) per-channel bands of 3 rows: the 8B gate_up at
+// M = 32768 +5 % against 4 rows (at M = 4096, 3 rows cost o 3 %).
 template <bool BLOCK>
-constexpr int band_rows() { return BLOCK ? 2 : 4; }
+__device__ __forceinline__ int band_rows(int tiles_m) {
+  return BLOCK ? 2 : (tiles_m >= 64 ? 3 : 4);
+}
 #ifndef FP8DQ_LINE_PERSIST
 #define FP8DQ_LINE_PERSIST 1
 #endif
@@ -155,7 +159,7 @@ __global__ __launch_bounds__((64 * LineCfg<BLOCK, BNP>::NW), 1) void gemm_prefil
   auto origin = [&](int v, int& m0, int& n0) {
     int bid = v;
     if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
-    constexpr int GM = band_rows<BLOCK>();
+    const int GM = band_rows<BLOCK>(tiles_m);
     const int group = GM * tiles_n;
     const int first_m = (bid / group) * GM;
     const int gm = min(tiles_m - first_m, GM);
