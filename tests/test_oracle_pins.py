@@ -295,6 +295,30 @@ def check_block_equals_channel(o, seed=6):
     assert np.allclose(y_b, y_c, rtol=1e-13, atol=0)
 
 
+def check_tolerance(o):
+    """The comparison of bf16 outputs: |y - y_ref| <= 1e-3 + 1e-2 |y_ref|
+    (spec tolerance), measured from the exact value y_ref. Values just
+    inside the bound pass, values just outside fail; the bound scales with
+    |y_ref|, not with the value under test."""
+    cases = [  # (y_ref, y, expected)
+        (0.0, 1e-3 * (1 - 1e-9), True), (0.0, -1e-3 * (1 - 1e-9), True),
+        (0.0, 1e-3 * (1 + 1e-6), False), (0.0, 5e-3, False),
+        (10.0, 10.101 - 1e-9, True), (10.0, 10.101 + 1e-6, False),
+        (10.0, 9.899 + 1e-9, True), (10.0, 9.899 - 1e-6, False),
+        (-3.0, -3.031 + 1e-9, True), (-3.0, -3.031 - 1e-6, False),
+        # 0.98905 is 0.01095 from 1.0: inside 1e-3 + 1e-2 * |y_ref| = 0.011,
+        # outside a bound taken from |y| (0.0108905)
+        (1.0, 0.98905, True),
+        (1e6, 1e6 * 1.01, True), (1e6, 1e6 * 1.0101, False),
+    ]
+    ref = np.array([c[0] for c in cases])
+    got = np.array([c[1] for c in cases])
+    want = np.array([c[2] for c in cases])
+    res = o.within_tolerance(got, ref)
+    assert res.dtype == bool and res.shape == ref.shape
+    assert np.array_equal(res, want), np.argwhere(res != want).ravel()
+
+
 def check_storage_closed_form(o):
     """Per-output-channel scales reproduce the 70B checkpoint figures."""
     g = json.load(open(os.path.join(GOLD, "llama31_70b_fp8_storage.json")))
@@ -320,7 +344,7 @@ CHECKS = [check_format_limits, check_decode_vs_torch, check_roundtrip,
           check_quantizer_exact_rational, check_scale_exhaustive,
           check_row_invariants, check_tiny_gemm_bruteforce,
           check_block_bruteforce, check_gemm_exact_int, check_lossless_linear,
-          check_block_equals_channel, check_storage_closed_form]
+          check_block_equals_channel, check_storage_closed_form, check_tolerance]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=lambda f: f.__name__)
@@ -359,6 +383,15 @@ def _no_sign_of_zero(v):
     return np.where((c & 0x7F) == 0, 0, c).astype(np.uint8)
 
 MUTATIONS = {
+    "tolerance_from_tested_value": ("within_tolerance",
+                                    lambda g, r, rtol=1e-2, atol=1e-3: np.abs(np.asarray(g) - r)
+                                    <= atol + rtol * np.abs(np.asarray(g))),
+    "tolerance_rtol_atol_swapped": ("within_tolerance",
+                                    lambda g, r, rtol=1e-2, atol=1e-3: np.abs(np.asarray(g) - r)
+                                    <= rtol + atol * np.abs(np.asarray(r))),
+    "tolerance_strict_relative": ("within_tolerance",
+                                  lambda g, r, rtol=1e-2, atol=1e-3: np.abs(np.asarray(g) - r)
+                                  <= rtol * np.abs(np.asarray(r))),
     "ties_away_from_zero": ("e4m3_encode", _ties_away),
     "truncation": ("e4m3_encode", _truncating),
     "drops_sign_of_zero": ("e4m3_encode", _no_sign_of_zero),
