@@ -46,23 +46,22 @@ PER_SOURCE = {
 }
 
 
-def _compile(src: str, build_dir: str = BUILD, defines=()) -> str:
+def _compile(src: str, build_dir: str = BUILD) -> str:
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     extra = PER_SOURCE.get(os.path.basename(src), [])
-    cmd = [HIPCC, *COMMON, *extra, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False, out: str = LIB, build_dir: str = BUILD,
-          defines=()) -> str:
+def build(verbose: bool = False, out: str = LIB, build_dir: str = BUILD) -> str:
     """Compile every source and link `out` (default: the in-tree library)."""
     os.makedirs(build_dir, exist_ok=True)
     srcs = _sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), srcs))
+        objs = list(ex.map(lambda s: _compile(s, build_dir), srcs))
     tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

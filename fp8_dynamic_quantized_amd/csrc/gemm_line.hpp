@@ -30,15 +30,8 @@ template <bool BLOCK>
 __device__ __forceinline__ int band_rows(int tiles_m) {
   return BLOCK ? 2 : (tiles_m >= 64 ? 3 : 4);
 }
-#ifndef FP8DQ_LINE_PERSIST
-#define FP8DQ_LINE_PERSIST 1
-#endif
-#ifndef FP8DQ_LINE_GF_AT
-#define FP8DQ_LINE_GF_AT 2   // block: odd-step MFMA slot where the next group's factor is formed
-#endif
-#ifndef FP8DQ_LINE_EARLY
-#define FP8DQ_LINE_EARLY 1
-#endif
+// block: odd-step MFMA slot at which the next group's factor is formed
+constexpr int kGroupFactorAt = 2;
 // s_waitcnt immediate (gfx9 encoding): at most n vector-memory operations of
 // this wave outstanding (expcnt / lgkmcnt not waited on).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
@@ -354,7 +347,7 @@ __global__ __launch_bounds__((64 * LineCfg<BLOCK, BNP>::NW), 1) void gemm_prefil
   // (every wave's part of it landed), and its first-half reads. Measured:
   // 8B qkv 96 against 101 us; with 256-wide tiles the second barrier per
   // pair costs more than the earlier refill gains (gate_up 400 against 388).
-  constexpr bool EARLY = !BLOCK && BNP == 192 && FP8DQ_LINE_EARLY;
+  constexpr bool EARLY = !BLOCK && BNP == 192;
   constexpr int TB = (NR + 1) / 2;                          // even: reads before the barrier
   constexpr int IPE = (NLD + NSC + (NM - TB) - 1) / (NM - TB);  // loads per slot after it
   constexpr int TW = NM / 2;                                // odd: MFMAs before the wait
@@ -372,7 +365,6 @@ __global__ __launch_bounds__((64 * LineCfg<BLOCK, BNP>::NW), 1) void gemm_prefil
       asm volatile("s_barrier" ::: "memory");
       if constexpr (BLOCK) {
         group_scales(kt / 2 + 1, ns);
-        if (FP8DQ_LINE_GF_AT < 0) group_factor();
       }
     }
     const int rs = cur == 0 ? cs : ns;
@@ -425,8 +417,8 @@ __global__ __launch_bounds__((64 * LineCfg<BLOCK, BNP>::NW), 1) void gemm_prefil
           }
         }
       }
-      if constexpr (BLOCK && cur == 1 && FP8DQ_LINE_GF_AT >= 0) {
-        if (more && t == FP8DQ_LINE_GF_AT) group_factor();
+      if constexpr (BLOCK && cur == 1) {
+        if (more && t == kGroupFactorAt) group_factor();
       }
       const int i = t / DMJ, j = t % DMJ;
       if constexpr (first) {
@@ -566,12 +558,10 @@ void launch_line(const uint8_t* qx, const float* sx, const uint8_t* qw, const fl
   // assignment balanced the CUs better than a fixed one (6 % slower
   // persistent).
   int grid = ntiles;
-#if FP8DQ_LINE_PERSIST
   if (!BLOCK || BNP == 256) {
     const int ncu = cu_count();
     if (ncu > 0 && ncu % 8 == 0 && ntiles > ncu) grid = ncu;
   }
-#endif
   hipLaunchKernelGGL((gemm_prefill_line_kernel<BLOCK, BNP>), dim3((unsigned)grid), dim3(64 * C::NW),
                      C::smem(K), st, qx, sx, qw, sw, (uint16_t*)y, (int)M, (int)N, (int)K,
                      (int)ldy, tiles_m, tiles_n);

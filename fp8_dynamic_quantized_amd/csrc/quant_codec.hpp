@@ -1,5 +1,5 @@
 // Exact dynamic E4M3 codec shared by the quantization kernels and the fused
-// decode kernel (same arithmetic everywhere, so codes agree bit for bit).
+// producers (same arithmetic everywhere, so codes agree bit for bit).
 //
 // What is computed (Llama-3.1-8B-Instruct-FP8-Dynamic page, FP8 dynamic
 // quantization table; E4M3 limits from the "Llama 3 精读实录" page, §2.1):
