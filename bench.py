@@ -433,7 +433,7 @@ def bench_long_small(F, torch):
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     qx = torch.empty((M, K), dtype=torch.uint8, device="cuda")
     sx = torch.empty((M,), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(16, F.fp8_workspace_bytes(M, N, K)), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(16, F.fp8_workspace_bytes(M, N, K)), dtype=torch.uint8, device="cuda")
     it = [0]
 
     def run():

@@ -152,7 +152,7 @@ def _workspace(M, N, K, block, flags, ws, device):
     import torch
     need = fp8_workspace_bytes(M, N, K, block, flags)
     if need and ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        ws = torch.zeros(need, dtype=torch.uint8, device=device)   # counters start at zero
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     return ws, nbytes
 

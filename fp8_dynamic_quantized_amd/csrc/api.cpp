@@ -32,13 +32,21 @@ inline bool use_decode(int64_t M, uint32_t flags) {
 }
 
 // Workspace for a GEMM call: the decode path processes M in slabs of at
-// most 64 rows (one after another on the stream), so one slab's partials.
+// most 64 rows (one after another on the stream), so the larger of a full
+// slab's and the last slab's needs.
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, uint32_t flags) {
-  if (M <= 0 || N <= 0 || K <= 0 || (K % 128) != 0) return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || (K % 128) != 0 || K > FP8DQ_MAX_K) return 0;
   if (!use_decode(M, flags)) return 0;
-  const int64_t slab = M < FP8DQ_DECODE_MAX_M ? M : FP8DQ_DECODE_MAX_M;
-  const DecodePlan p = fp8dq::plan_decode(slab, N, K);
-  return fp8dq::decode_workspace_bytes(slab, N, p);
+  size_t need = 0;
+  const int64_t slabs[2] = {M < FP8DQ_DECODE_MAX_M ? M : FP8DQ_DECODE_MAX_M,
+                            M % FP8DQ_DECODE_MAX_M};
+  for (int64_t slab : slabs) {
+    if (slab <= 0) continue;
+    const DecodePlan p = fp8dq::plan_decode(slab, N, K);
+    const size_t b = fp8dq::decode_workspace_bytes(slab, N, p);
+    if (b > need) need = b;
+  }
+  return need;
 }
 
 int check_gemm_args(const uint8_t* qx, const float* sx, const uint8_t* qw,
@@ -50,9 +58,11 @@ int check_gemm_args(const uint8_t* qx, const float* sx, const uint8_t* qw,
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return FP8DQ_ERR_SHAPE;
   if (!known_flags(flags)) return FP8DQ_ERR_FLAGS;
   // the prefill and whole-line decode kernels address the weight operand
-  // with 32-bit byte offsets, and the prefill path runs X in blocks of whole
-  // 256-row tiles that fit them (K < 2^24)
-  if (N * K >= (int64_t(1) << 32) || K >= (int64_t(1) << 24)) return FP8DQ_ERR_SHAPE;
+  // with 32-bit byte offsets (N * K < 2^32), and the prefill path runs X in
+  // blocks of whole 256-row tiles that fit them; K is at most
+  // FP8DQ_MAX_K, the range over which the accumulation error is validated
+  // (and the block kernel keeps a tile's weight-block scales in LDS)
+  if (N * K >= (int64_t(1) << 32) || K > FP8DQ_MAX_K) return FP8DQ_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8DQ_OK;
   if (!qx || !sx || !qw || !sw || !y) return FP8DQ_ERR_NULL;
   if (!aligned16(qx) || !aligned16(sx) || !aligned16(qw) || !aligned16(sw) ||
@@ -94,8 +104,8 @@ int run_gemm(const uint8_t* qx, const float* sx, const uint8_t* qw,
     const DecodePlan p = fp8dq::plan_decode(rows, N, K);
     const float* sxs = sx + (block ? m0 * G : m0);
     fp8dq::launch_gemm_decode(qx + m0 * K, sxs, qw, sw,
-                              static_cast<uint16_t*>(y) + m0 * N,
-                              static_cast<float*>(ws), rows, N, K, block, p, st);
+                              static_cast<uint16_t*>(y) + m0 * N, ws, rows, N, K,
+                              block, p, st);
     const int s = launch_status();
     if (s != FP8DQ_OK) return s;
   }

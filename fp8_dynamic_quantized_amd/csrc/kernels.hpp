@@ -28,18 +28,24 @@ void launch_gemm_prefill(const uint8_t* qx, const float* sx, const uint8_t* qw,
                          const float* sw, void* y, int64_t M, int64_t N,
                          int64_t K, bool block, hipStream_t st);
 
-// Decode GEMM (gemm_decode.hip): small-M, HBM-streaming, split-K.
+// Decode GEMM (gemm_decode.hip): small-M, HBM-streaming, split-K with the
+// reduction done by the last slice of each output tile.
 struct DecodePlan {
   int mb;            // 16-row blocks of M covered (M <= 16 * mb)
-  int nb;            // 16-row blocks of N per workgroup
   int splits;        // K slices across the grid (1: no partials)
   int kt_per_split;  // 128-wide K steps per slice
   int line;          // 1: whole-line kernel (LDS ring), 0: register-loading kernel
 };
+// Split workspaces: [tile counters: kDecodeCounterBytes][fp32 partials
+// splits x M x N]. The counters must be zero before a call and every call
+// leaves them zero; K is split only while a launch has at most
+// kDecodeMaxSplitTiles output tiles, so the counter area never moves.
+constexpr int64_t kDecodeMaxSplitTiles = 4096;
+constexpr size_t kDecodeCounterBytes = (size_t)kDecodeMaxSplitTiles * 4;
 DecodePlan plan_decode(int64_t M, int64_t N, int64_t K);
 size_t decode_workspace_bytes(int64_t M, int64_t N, const DecodePlan& p);
 void launch_gemm_decode(const uint8_t* qx, const float* sx, const uint8_t* qw,
-                        const float* sw, void* y, float* ws, int64_t M,
+                        const float* sw, void* y, void* ws, int64_t M,
                         int64_t N, int64_t K, bool block, const DecodePlan& p,
                         hipStream_t st);
 

@@ -26,7 +26,24 @@
  *   y     = bf16_RNE( sum_k val(qx[m,k]) val(qw[n,k]) * sx[m] * sw[n] )
  *   block: y = bf16_RNE( sum_g (sum_{k in g} val*val) * sx[m,g] * sw[n/128,g] )
  *   The sum is accumulated in fp32 (any order); codes and scales are
- *   bit-exact, y is within 1e-2 relative / 1e-3 absolute of the exact value.
+ *   bit-exact, y is within 1e-2 relative / 1e-3 absolute of the exact value
+ *   on the workloads the tests cover (see "Accumulation" below).
+ *
+ * Accumulation (measured on gfx950, both FP8 MFMA shapes): the matrix
+ * instruction adds its products in groups of 8 consecutive k. Inside a
+ * group every product is cut toward zero to a multiple of 2^(E - 13), E the
+ * largest e(x) + e(w) of the group (unbiased exponents, -6 for subnormal
+ * codes); groups and the running fp32 sum are then added with about 24
+ * significant bits. So per output
+ *     |acc - exact| < sum over groups g of 7 * 2^(E_g - 13)  (+ fp32 terms),
+ * the bound being reached only where a group mixes products more than 7
+ * binades apart. The decode path (FP8DQ_FORCE_DECODE, and M <= 64 under
+ * FP8DQ_AUTO) splits each token row's codes of magnitude >= 16 from the
+ * rest and runs the two halves through separate MFMAs, so large activation
+ * codes (outlier channels) do not cut the small ones' products; the prefill
+ * kernels keep one MFMA per product (their rate is the matrix core's).
+ * K is at most FP8DQ_MAX_K: the range over which these errors were
+ * measured against the exact sum.
  *
  * Conventions for every entry point:
  *   - extern "C"; no C++ exception crosses the boundary.
@@ -73,6 +90,10 @@ extern "C" {
 /* Largest M the decode (small-M) path takes under FP8DQ_AUTO. */
 #define FP8DQ_DECODE_MAX_M   64
 
+/* Largest K of the GEMM and linear calls (2^17; the longest Llama-3.x
+ * reduction is 28672). */
+#define FP8DQ_MAX_K          131072
+
 /*
  * fp8_quant_act -- dynamic activation quantization (also the per-channel
  * weight quantizer: rows of W are output channels, same arithmetic).
@@ -105,14 +126,24 @@ int fp8_quant_weight_block(const void* w_bf16, int64_t N, int64_t K,
                            uint8_t* qw, float* sw, void* stream);
 
 /*
- * fp8_gemm -- Y = bf16( (Qx Qw^T) * sx[m] * sw[n] ) from codes and scales.
+ * fp8_gemm -- Y = bf16( (Qx Qw^T) * sx[m] * sw[n] ) from codes and scales:
+ * the FP8 matrix product with per-token activation scales and per-output-
+ * channel weight scales, rescaled to bf16 in the epilogue.
+ * Source: FP8 dynamic quantization table of the Llama-3.1-8B-Instruct-FP8-
+ * Dynamic page (per-channel weights, per-token activations); the
+ * Llama-3.1-70B-FP8-Dynamic page, section 1.2 (the same scheme) and section
+ * 3 (the FP8 products run on the matrix units, no dequantized copy).
  *   qx : uint8 [M, K], sx : fp32 [M];  qw : uint8 [N, K], sw : fp32 [N]
  *   y  : bf16 [M, N] (output)
  *   flags : FP8DQ_AUTO / FP8DQ_FORCE_PREFILL / FP8DQ_FORCE_DECODE
- *   ws, ws_bytes : device workspace for split-K partial sums; ws may be
- *        NULL iff fp8_workspace_bytes(M, N, K, 0, flags) == 0.
- * Size rules: M, N >= 0; K > 0, K % 128 == 0 and K < 2^24; N * K < 2^32
- * (the weight codes under 4 GiB); FP8DQ_ERR_SHAPE otherwise.
+ *   ws, ws_bytes : device workspace for split-K partial sums and tile
+ *        counters; ws may be NULL iff fp8_workspace_bytes(M, N, K, 0, flags)
+ *        == 0. Its bytes must be zero before the first call that uses it
+ *        (allocate it zero-filled); every call leaves its counter area zero
+ *        again, so a zeroed workspace serves any number of calls of any
+ *        shapes, one at a time (calls that overlap on one workspace race).
+ * Size rules: M, N >= 0; K > 0, K % 128 == 0 and K <= FP8DQ_MAX_K;
+ * N * K < 2^32 (the weight codes under 4 GiB); FP8DQ_ERR_SHAPE otherwise.
  */
 int fp8_gemm(const uint8_t* qx, const float* sx, const uint8_t* qw,
              const float* sw, void* y_bf16, int64_t M, int64_t N, int64_t K,
@@ -122,9 +153,12 @@ int fp8_gemm(const uint8_t* qx, const float* sx, const uint8_t* qw,
  * fp8_gemm_block -- block-scaled GEMM:
  *   y[m,n] = bf16( sum_g P_g[m,n] * sx[m,g] * sw[n/128, g] ), P_g the code
  *   product summed over the g-th 128-column group.
+ * Source: FP8 block quantization table of the Llama-3.2-3B-Instruct-FP8-
+ * Block page (weight block structure [128, 128], activations per token per
+ * group of 128, dynamic).
  *   sx : fp32 [M, K/128];  sw : fp32 [N/128, K/128]
  * Size rules: M, N >= 0; N % 128 == 0; K > 0, K % 128 == 0 and
- * K < 2^24; N * K < 2^32, as for fp8_gemm.
+ * K <= FP8DQ_MAX_K; N * K < 2^32, as for fp8_gemm.
  * ws as for fp8_gemm (block = 1 in fp8_workspace_bytes).
  */
 int fp8_gemm_block(const uint8_t* qx, const float* sx, const uint8_t* qw,
@@ -136,8 +170,13 @@ int fp8_gemm_block(const uint8_t* qx, const float* sx, const uint8_t* qw,
  * fp8_linear -- the FP8-Dynamic linear: quantize X per token (writes qx_out,
  * sx_out, which the caller owns and may inspect) and run fp8_gemm with the
  * pre-quantized weight (qw, sw from fp8_quant_act on W).
+ * Source: the FP8 dynamic quantization table of the Llama-3.1-8B-Instruct-
+ * FP8-Dynamic page (weights static per channel, activations dynamic per
+ * token, computed at run time) and the Llama-3.1-70B-FP8-Dynamic page,
+ * section 1.2 (the same split: weights quantized once, activations per
+ * inference).
  *   x : bf16 [M, K]; qx_out : uint8 [M, K]; sx_out : fp32 [M]
- * Size rules: those of fp8_gemm.
+ * Size rules, workspace and errors: those of fp8_gemm.
  */
 int fp8_linear(const void* x_bf16, const uint8_t* qw, const float* sw,
                void* y_bf16, int64_t M, int64_t N, int64_t K,
@@ -148,7 +187,10 @@ int fp8_linear(const void* x_bf16, const uint8_t* qw, const float* sw,
  * fp8_linear_block -- block variant: quantize X per token per 128-group
  * (qx_out uint8 [M, K], sx_out fp32 [M, K/128]) then fp8_gemm_block with
  * block-quantized weights (qw, sw from fp8_quant_weight_block).
- * Size rules: those of fp8_gemm_block.
+ * Source: FP8 block quantization table of the Llama-3.2-3B-Instruct-FP8-
+ * Block page (block_structure [128, 128] weights; group-128 dynamic
+ * activations).
+ * Size rules, workspace and errors: those of fp8_gemm_block.
  */
 int fp8_linear_block(const void* x_bf16, const uint8_t* qw, const float* sw,
                      void* y_bf16, int64_t M, int64_t N, int64_t K,

@@ -77,9 +77,13 @@ def test_gemm_errors(L, fn):
     assert g(A, A, A, A, A, 16, 1 << 16, 1 << 16, 1, None, 0, None) == -2
     assert g(A, A, A, A, A, 32, 1 << 16, 1 << 16, 0, None, 0, None) == -2
     assert g(A, A, A, A, A, 1, 1 << 16, 1 << 16, 2, None, 0, None) == -2
-    # K from 2^24 (a 256-row block of X codes would pass 4 GiB)
-    assert g(A, A, A, A, A, 65536, 128, 1 << 24, 0, None, 0, None) == -2
-    assert g(A, A, A, A, A, 16, 128, 1 << 24, 0, None, 0, None) == -2
+    # K beyond FP8DQ_MAX_K = 2^17 (the range the accumulation error is
+    # validated over) is rejected on every path; 2^17 itself is accepted
+    for flags in (0, 1, 2):
+        assert g(A, A, A, A, A, 65536, 128, 1 << 24, flags, None, 0, None) == -2
+        assert g(A, A, A, A, A, 16, 128, (1 << 17) + 128, flags, None, 0, None) == -2
+        assert g(A, A, A, A, A, 4096, 128, (1 << 17) + 128, flags, None, 0, None) == -2
+    assert g(A, A, A, A, A, 16, 128, 1 << 17, 0, None, 0, None) != -2
 
 
 def test_gemm_block_needs_n_multiple_of_128(L):
@@ -88,22 +92,27 @@ def test_gemm_block_needs_n_multiple_of_128(L):
 
 
 def test_workspace_rules(L):
-    # a small-N decode shape with long rows splits K and needs a workspace;
-    # with short rows (K < 16384) it runs unsplit; prefill needs none
-    need = F.fp8_workspace_bytes(16, 1024, 16384)
-    assert need > 0 and need % 4 == 0
-    assert F.fp8_workspace_bytes(16, 1024, 4096) == 0
+    # decode shapes whose row blocks leave the CUs short of work split K and
+    # need a workspace: a zeroed counter area of 16 KiB, then fp32 partials
+    # (splits x M x N); prefill needs none
+    for M, N, K in [(16, 1024, 16384), (1, 10240, 8192), (64, 8192, 28672), (20, 100, 65536)]:
+        need = F.fp8_workspace_bytes(M, N, K)
+        assert need >= 16384 + 2 * 4 * M * N and (need - 16384) % (4 * M * N) == 0, (M, N, K)
+    assert F.fp8_workspace_bytes(1, 57344, 8192) == 0         # enough row blocks: no split
     assert F.fp8_workspace_bytes(4096, 4096, 4096) == 0
     assert F.fp8_workspace_bytes(16, 1024, 16384, flags=F.FORCE_PREFILL) == 0
     assert F.fp8_workspace_bytes(16, 1024, 100) == 0       # invalid K -> 0
+    assert F.fp8_workspace_bytes(16, 1024, (1 << 17) + 128) == 0   # K beyond the bound -> 0
     assert F.fp8_workspace_bytes(16, 1000, 4096, block=True) == 0  # invalid N
+    need = F.fp8_workspace_bytes(16, 1024, 16384)
     g = L.fp8_gemm
     assert g(A, A, A, A, A, 16, 1024, 16384, 0, None, 0, None) == -1
     assert g(A, A, A, A, A, 16, 1024, 16384, 0, A, need - 4, None) == -4
     assert g(A, A, A, A, A, 16, 1024, 16384, 0, MIS, need, None) == -3
-    # M beyond one decode slab uses the slab's workspace size
-    assert F.fp8_workspace_bytes(200, 1024, 4096, flags=F.FORCE_DECODE) == \
-        F.fp8_workspace_bytes(64, 1024, 4096)
+    # M beyond one decode slab (64 rows) takes the larger of a full slab's and
+    # the last slab's workspace
+    assert F.fp8_workspace_bytes(200, 1024, 16384, flags=F.FORCE_DECODE) == max(
+        F.fp8_workspace_bytes(64, 1024, 16384), F.fp8_workspace_bytes(8, 1024, 16384))
 
 
 @pytest.mark.parametrize("fn", ["fp8_linear", "fp8_linear_block"])
