@@ -34,7 +34,8 @@ inline bool use_decode(int64_t M, uint32_t flags) {
 // Workspace for a GEMM call: the decode path processes M in slabs of at
 // most 64 rows (one after another on the stream), so the larger of a full
 // slab's and the last slab's needs.
-size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, uint32_t flags) {
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, uint32_t flags,
+                     size_t cap = SIZE_MAX) {
   if (M <= 0 || N <= 0 || K <= 0 || (K % 128) != 0 || K > FP8DQ_MAX_K) return 0;
   if (!use_decode(M, flags)) return 0;
   size_t need = 0;
@@ -42,7 +43,7 @@ size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, uint32_t flags) {
                             M % FP8DQ_DECODE_MAX_M};
   for (int64_t slab : slabs) {
     if (slab <= 0) continue;
-    const DecodePlan p = fp8dq::plan_decode(slab, N, K);
+    const DecodePlan p = fp8dq::plan_decode(slab, N, K, cap);
     const size_t b = fp8dq::decode_workspace_bytes(slab, N, p);
     if (b > need) need = b;
   }
@@ -52,7 +53,7 @@ size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, uint32_t flags) {
 int check_gemm_args(const uint8_t* qx, const float* sx, const uint8_t* qw,
                     const float* sw, const void* y, int64_t M, int64_t N,
                     int64_t K, uint32_t flags, const void* ws, size_t ws_bytes,
-                    bool block) {
+                    bool block, bool check_ws = true) {
   if (M < 0 || N < 0 || K <= 0 || (K % 128) != 0) return FP8DQ_ERR_SHAPE;
   if (block && (N % 128) != 0) return FP8DQ_ERR_SHAPE;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return FP8DQ_ERR_SHAPE;
@@ -68,7 +69,7 @@ int check_gemm_args(const uint8_t* qx, const float* sx, const uint8_t* qw,
   if (!aligned16(qx) || !aligned16(sx) || !aligned16(qw) || !aligned16(sw) ||
       !aligned16(y))
     return FP8DQ_ERR_ALIGN;
-  const size_t need = gemm_ws_bytes(M, N, K, flags);
+  const size_t need = check_ws ? gemm_ws_bytes(M, N, K, flags) : 0;
   if (need > 0) {
     if (!ws) return FP8DQ_ERR_NULL;
     if (!aligned16(ws)) return FP8DQ_ERR_ALIGN;
@@ -78,9 +79,13 @@ int check_gemm_args(const uint8_t* qx, const float* sx, const uint8_t* qw,
 }
 
 // Launch a validated GEMM (M, N > 0).
+// ws_cap: the workspace the decode plans may use (the caller's workspace was
+// checked against the uncapped need; the no-allocation entry point caps the
+// plans at its static scratch).
 int run_gemm(const uint8_t* qx, const float* sx, const uint8_t* qw,
              const float* sw, void* y, int64_t M, int64_t N, int64_t K,
-             uint32_t flags, void* ws, bool block, hipStream_t st) {
+             uint32_t flags, void* ws, bool block, hipStream_t st,
+             size_t ws_cap = SIZE_MAX) {
   if (!use_decode(M, flags)) {
     // The prefill kernels address an operand with 32-bit byte offsets: run
     // row blocks of X small enough for that (W itself must stay below 4 GiB,
@@ -101,7 +106,7 @@ int run_gemm(const uint8_t* qx, const float* sx, const uint8_t* qw,
   const int64_t G = K / 128;
   for (int64_t m0 = 0; m0 < M; m0 += FP8DQ_DECODE_MAX_M) {
     const int64_t rows = (M - m0) < FP8DQ_DECODE_MAX_M ? (M - m0) : FP8DQ_DECODE_MAX_M;
-    const DecodePlan p = fp8dq::plan_decode(rows, N, K);
+    const DecodePlan p = fp8dq::plan_decode(rows, N, K, ws_cap);
     const float* sxs = sx + (block ? m0 * G : m0);
     fp8dq::launch_gemm_decode(qx + m0 * K, sxs, qw, sw,
                               static_cast<uint16_t*>(y) + m0 * N, ws, rows, N, K,

@@ -86,11 +86,22 @@ __device__ __forceinline__ v8i gload_frag(const uint8_t* p) {
   return r;
 }
 
-__device__ __forceinline__ void st_part(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Split-K partial tiles: every (tile, slice) owns a contiguous block of the
+// workspace in the lanes' own order (16 bytes per lane and fragment), so a
+// wave's store or load of a fragment is one coalesced 1 KB access. Stores and
+// loads carry the sc1 cache policy (as agent-scope atomic accesses do): they
+// reach the memory side of the per-XCD L2s, where another XCD's slice reads
+// them.
+constexpr int kSc1 = 16;   // cache-policy operand bit: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ float ld_part(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void st_part(__amdgpu_buffer_rsrc_t r, uint32_t off, const v4f& v) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, (int)off, 0, kSc1);
+}
+__device__ __forceinline__ v4f ld_part(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kSc1));
 }
 
 // y[m, n..n+3] = bf16(v * scales) (per-channel: sx[m] * sw[n+r]; block: v is
@@ -224,24 +235,24 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
     }
     return;
   }
-  // split K: publish this slice's partial, count it, the last slice sums
-  if (live) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (n + r < N) st_part(part + ((int64_t)split * M + m) * N + n + r, s[r]);
-  }
+  // split K: publish this slice's partial tile (1 KB, lane order), count it;
+  // the last slice adds all slices' tiles in slice order
+  float* tile = part + (int64_t)blockIdx.x * splits * 256;
+  const __amdgpu_buffer_rsrc_t pr = part_rsrc(tile, (uint32_t)splits * 1024u);
+  st_part(pr, (uint32_t)split * 1024u + (uint32_t)lane * 16u, s);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the partial's stores have completed
   unsigned old = 0;
   if (lane == 0)
     old = __hip_atomic_fetch_add(cnt + blockIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (__shfl(old, 0) != (unsigned)(splits - 1)) return;
-  if (live) {
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < splits; ++k) {
+  v4f t = ld_part(pr, (uint32_t)lane * 16u);
+  for (int k = 1; k < splits; ++k) {
+    const v4f o = ld_part(pr, (uint32_t)k * 1024u + (uint32_t)lane * 16u);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        v[r] += ld_part(part + ((int64_t)k * M + m) * N + min(n + r, N - 1));
-    }
+    for (int r = 0; r < 4; ++r) t[r] += o[r];
+  }
+  if (live) {
+    const float v[4] = {t[0], t[1], t[2], t[3]};
     store_out<BLOCK>(y, sx, sw, m, n, N, v);
   }
   if (lane == 0)
@@ -413,19 +424,18 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_line_kernel(
     }
     return;
   }
-  // split K: publish this slice's partial tile, count it, the last slice sums
+  // split K: publish this slice's partial tile (lane order: [wave][i][j]
+  // [lane] x 16 bytes), count it; the last slice adds all slices' tiles in
+  // slice order
+  constexpr uint32_t TILE_B = 4u * 2u * MB * 1024u;   // bytes of one slice's tile
+  float* tile = part + (int64_t)blockIdx.x * splits * (TILE_B / 4);
+  const __amdgpu_buffer_rsrc_t pr = part_rsrc(tile, (uint32_t)splits * TILE_B);
+  const uint32_t lo_off = (uint32_t)wave * 2u * MB * 1024u + (uint32_t)lane * 16u;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int n = n0 + 32 * wave + 16 * i + 4 * kq;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < MB; ++j) {
-      const int m = 16 * j + fr;
-      if (n >= N || m >= M) continue;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (n + r < N) st_part(part + ((int64_t)split * M + m) * N + n + r, acc[i][j][r]);
-    }
-  }
+    for (int j = 0; j < MB; ++j)
+      st_part(pr, (uint32_t)split * TILE_B + lo_off + (uint32_t)(i * MB + j) * 1024u, acc[i][j]);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's stores have completed
   __syncthreads();                            // ... and every other wave's
   if (tid == 0)
@@ -433,6 +443,27 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_line_kernel(
                                        __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(splits - 1);
   __syncthreads();
   if (!last_flag) return;
+  // slice by slice, all of a slice's fragments in flight together (and the
+  // next slice's issued before this one's adds): about one memory latency
+  // per slice
+  v4f nxt[2][MB];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < MB; ++j) acc[i][j] = ld_part(pr, lo_off + (uint32_t)(i * MB + j) * 1024u);
+  for (int k = 1; k < splits; ++k) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < MB; ++j)
+        nxt[i][j] = ld_part(pr, (uint32_t)k * TILE_B + lo_off + (uint32_t)(i * MB + j) * 1024u);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < MB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] += nxt[i][j][r];
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int n = n0 + 32 * wave + 16 * i + 4 * kq;
@@ -441,12 +472,7 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_line_kernel(
     for (int j = 0; j < MB; ++j) {
       const int m = 16 * j + fr;
       if (m >= M) continue;
-      float v[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int k = 0; k < splits; ++k) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          v[r] += ld_part(part + ((int64_t)k * M + m) * N + min(n + r, N - 1));
-      }
+      const float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
       store_out<BLOCK>(y, sx, sw, m, n, N, v);
     }
   }
@@ -492,15 +518,7 @@ int decode_cu_count() {
 
 }  // namespace
 
-// Split counts are chosen with a cost model in bytes per CU:
-//   rounds x bytes per work item / rate + partials written and read,
-// where rounds = ceil(items / CUs), an item is one row block x one K slice,
-// and the rate falls below 1 while a CU holds fewer items than keep its
-// loads in flight (3 register-kernel workgroups or 2 whole-line ones). The
-// model reproduces the split counts measured best in isolation: the 70B down
-// (K = 28672) at 32 and 64 tokens in 8 slices, the 70B qkv and o at one
-// token in 2.
-DecodePlan plan_decode(int64_t M, int64_t N, int64_t K) {
+DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, size_t ws_cap) {
   DecodePlan p;
   p.mb = (int)((M + 15) / 16);
   if (p.mb < 1) p.mb = 1;
@@ -509,24 +527,39 @@ DecodePlan plan_decode(int64_t M, int64_t N, int64_t K) {
   p.line = M > 16 ? 1 : 0;
   const int64_t KT = K / BK;
   const int64_t ncu = decode_cu_count();
-  const int64_t rows = p.line ? DL_BN : 16;
-  const int64_t RB = (N + rows - 1) / rows;
-  const double full_at = p.line ? 2.0 : 3.0;       // items per CU for the full rate
-  const double item_step_bytes = (double)rows * BK;
-  double best = 0.0;
-  int64_t best_s = 1;
-  for (int64_t s = 1; s <= 64; s *= 2) {
-    if (s > 1 && (KT / s < 8 || RB > kDecodeMaxSplitTiles)) break;
-    const int64_t kps = (KT + s - 1) / s;
-    const int64_t ns = (KT + kps - 1) / kps;
-    const int64_t items = RB * ns;
-    const double per_cu = (double)items / (double)ncu;
-    const double rate = per_cu >= full_at ? 1.0 : per_cu / full_at;
-    const double rounds = (double)((items + ncu - 1) / ncu);
-    double cost = rounds * (double)kps * item_step_bytes / rate;
-    if (ns > 1) cost += (double)ns * (double)M * (double)N * 8.0 / (double)ncu;
-    if (s == 1 || cost < best * 0.98) { best = cost; best_s = ns; }
+  if (p.line) {
+    // Whole-line kernel: 128 weight rows per workgroup, two workgroups per
+    // CU. Split K until there are >= 1.5 workgroups per CU, keeping at least
+    // 8 K steps per slice; long rows with fewer row blocks than CUs split to
+    // two workgroups per CU, where the slices' partial tiles are small next
+    // to the weights. (Measured on the 70B linears at 32 and 64 tokens: more
+    // slices than this lose more to the partial tiles and the last slice's
+    // reduction than they gain in balance.)
+    const int64_t wg0 = (N + DL_BN - 1) / DL_BN;
+    const int64_t target = (K >= 16384 && wg0 < ncu) ? 2 * ncu : (3 * ncu) / 2;
+    int64_t sp = (target + wg0 - 1) / wg0;
+    if (sp > KT / 8) sp = KT / 8;
+    if (sp < 1) sp = 1;
+    const size_t tile_b = (size_t)DL_BN * 16 * p.mb * 4;
+    while (sp > 1 && (wg0 > kDecodeMaxSplitTiles ||
+                      kDecodeCounterBytes + (size_t)sp * (size_t)wg0 * tile_b > ws_cap))
+      --sp;
+    p.kt_per_split = (int)((KT + sp - 1) / sp);
+    p.splits = (int)((KT + p.kt_per_split - 1) / p.kt_per_split);
+    return p;
   }
+  // Register kernel: 16 weight rows per workgroup. K is split only for long
+  // rows (K >= 16384) with fewer row blocks than CUs, into the fewest slices
+  // that give every CU one (at least 8 K steps each). Measured: on the 70B
+  // linears at 1 and 8 tokens (512 to 3584 row blocks) 2 or 4 slices were
+  // 0-13 % slower than none, and the 16-token 4096 -> 1024 linear (64 row
+  // blocks, 32 K steps) took 12.6 us in 4 slices against 11.1 us unsplit.
+  const int64_t RB = (N + 15) / 16;
+  int64_t best_s = 1;
+  while (K >= 16384 && RB * best_s < ncu && KT / (best_s * 2) >= 8 &&
+         RB <= kDecodeMaxSplitTiles &&
+         kDecodeCounterBytes + (size_t)(best_s * 2) * (size_t)RB * 1024u <= ws_cap)
+    best_s *= 2;
   p.kt_per_split = (int)((KT + best_s - 1) / best_s);
   p.splits = (int)((KT + p.kt_per_split - 1) / p.kt_per_split);
   return p;
@@ -534,7 +567,12 @@ DecodePlan plan_decode(int64_t M, int64_t N, int64_t K) {
 
 size_t decode_workspace_bytes(int64_t M, int64_t N, const DecodePlan& p) {
   if (p.splits <= 1) return 0;
-  return kDecodeCounterBytes + (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
+  (void)M;
+  // one partial tile per (tile, slice): 16 x 16 floats (register kernel) or
+  // 128 x 16 mb floats (whole-line kernel)
+  const size_t tiles = p.line ? (size_t)((N + DL_BN - 1) / DL_BN) : (size_t)((N + 15) / 16);
+  const size_t tile_b = p.line ? (size_t)DL_BN * 16 * p.mb * 4 : (size_t)16 * 16 * 4;
+  return kDecodeCounterBytes + (size_t)p.splits * tiles * tile_b;
 }
 
 void launch_gemm_decode(const uint8_t* qx, const float* sx, const uint8_t* qw,

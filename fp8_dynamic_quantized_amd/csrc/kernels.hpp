@@ -42,7 +42,9 @@ struct DecodePlan {
 // kDecodeMaxSplitTiles output tiles, so the counter area never moves.
 constexpr int64_t kDecodeMaxSplitTiles = 4096;
 constexpr size_t kDecodeCounterBytes = (size_t)kDecodeMaxSplitTiles * 4;
-DecodePlan plan_decode(int64_t M, int64_t N, int64_t K);
+// ws_cap: largest workspace the plan may use (split counts needing more are
+// not considered; one slice needs none).
+DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, size_t ws_cap = SIZE_MAX);
 size_t decode_workspace_bytes(int64_t M, int64_t N, const DecodePlan& p);
 void launch_gemm_decode(const uint8_t* qx, const float* sx, const uint8_t* qw,
                         const float* sw, void* y, void* ws, int64_t M,

@@ -95,10 +95,14 @@ def test_workspace_rules(L):
     # decode shapes whose row blocks leave the CUs short of work split K and
     # need a workspace: a zeroed counter area of 16 KiB, then fp32 partials
     # (splits x M x N); prefill needs none
-    for M, N, K in [(16, 1024, 16384), (1, 10240, 8192), (64, 8192, 28672), (20, 100, 65536)]:
+    # (partial tiles of 16 x 16 floats, or 128 x 16*ceil(M/16) floats)
+    for M, N, K in [(16, 1024, 16384), (1, 96, 131072), (64, 8192, 28672), (20, 100, 65536)]:
         need = F.fp8_workspace_bytes(M, N, K)
-        assert need >= 16384 + 2 * 4 * M * N and (need - 16384) % (4 * M * N) == 0, (M, N, K)
-    assert F.fp8_workspace_bytes(1, 57344, 8192) == 0         # enough row blocks: no split
+        assert need >= 16384 + 2 * 1024 and (need - 16384) % 1024 == 0, (M, N, K)
+    # up to 16 tokens, as many 16-row blocks as CUs or more: no split
+    assert F.fp8_workspace_bytes(1, 57344, 8192) == 0
+    assert F.fp8_workspace_bytes(8, 10240, 8192) == 0
+    assert F.fp8_workspace_bytes(16, 1024, 4096) == 0        # short rows: no split
     assert F.fp8_workspace_bytes(4096, 4096, 4096) == 0
     assert F.fp8_workspace_bytes(16, 1024, 16384, flags=F.FORCE_PREFILL) == 0
     assert F.fp8_workspace_bytes(16, 1024, 100) == 0       # invalid K -> 0
