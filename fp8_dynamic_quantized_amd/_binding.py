@@ -33,6 +33,8 @@ _SIGS = {
                                   ctypes.c_uint32, _c_p, ctypes.c_size_t, _c_p]),
     "fp8_linear_block": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _c_p,
                                         _c_p, ctypes.c_uint32, _c_p, ctypes.c_size_t, _c_p]),
+    "fp8_linear_noalloc": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _c_p,
+                                          _c_p, ctypes.c_uint32, _c_p]),
     "fp8_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, ctypes.c_int32, ctypes.c_uint32]),
     "fp8_silu_mul_quant": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p]),
     "fp8_rmsnorm_quant": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, ctypes.c_double, _c_p,
@@ -201,6 +203,27 @@ def fp8_linear(x, qw, sw, y=None, qx_out=None, sx_out=None, flags: int = AUTO,
     _check("fp8_linear", lib().fp8_linear(
         _ptr(x), _ptr(qw), _ptr(sw), _ptr(y), M, N, K, _ptr(qx_out), _ptr(sx_out),
         flags, _ptr(ws), nb, _stream(x, stream)))
+    return y, qx_out, sx_out
+
+
+def fp8_linear_noalloc(x, qw, sw, y=None, qx_out=None, sx_out=None, flags: int = AUTO,
+                       stream=None):
+    """fp8_linear without a workspace (the library's static device scratch).
+
+    Returns (y bf16 [M, N], qx uint8 [M, K], sx fp32 [M]); outputs not passed
+    are allocated here, by torch, before the call.
+    """
+    import torch
+    M, K = x.shape
+    N = qw.shape[0]
+    _need(x, torch.bfloat16, (M, K), "x")
+    dev = x.device
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    qx_out = torch.empty((M, K), dtype=torch.uint8, device=dev) if qx_out is None else qx_out
+    sx_out = torch.empty((M,), dtype=torch.float32, device=dev) if sx_out is None else sx_out
+    _check("fp8_linear_noalloc", lib().fp8_linear_noalloc(
+        _ptr(x), _ptr(qw), _ptr(sw), _ptr(y), M, N, K, _ptr(qx_out), _ptr(sx_out),
+        flags, _stream(x, stream)))
     return y, qx_out, sx_out
 
 

@@ -189,6 +189,31 @@ int fp8_linear(const void* x_bf16, const uint8_t* qw, const float* sw,
                        ws, ws_bytes, stream, false);
 }
 
+int fp8_linear_noalloc(const void* x_bf16, const uint8_t* qw, const float* sw,
+                       void* y_bf16, int64_t M, int64_t N, int64_t K,
+                       uint8_t* qx_out, float* sx_out, uint32_t flags, void* stream) {
+  int s = check_gemm_args(qx_out, sx_out, qw, sw, y_bf16, M, N, K, flags, nullptr, 0,
+                          false, /*check_ws=*/false);
+  if (s != FP8DQ_OK || M == 0 || N == 0) return s;
+  if (!x_bf16) return FP8DQ_ERR_NULL;
+  if (!aligned16(x_bf16)) return FP8DQ_ERR_ALIGN;
+  // the decode plans are capped at the static scratch, so the need never
+  // exceeds it; checked all the same before anything is enqueued
+  const size_t need = gemm_ws_bytes(M, N, K, flags, fp8dq::kScratchBytes);
+  if (need > fp8dq::kScratchBytes) return FP8DQ_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = fp8dq::scratch_for_current_device();
+    if (!ws) return FP8DQ_ERR_HIP;
+  }
+  hipStream_t st = as_stream(stream);
+  fp8dq::launch_quant_rows(x_bf16, M, K, qx_out, sx_out, st);
+  s = launch_status();
+  if (s != FP8DQ_OK) return s;
+  return run_gemm(qx_out, sx_out, qw, sw, y_bf16, M, N, K, flags, ws, false, st,
+                  fp8dq::kScratchBytes);
+}
+
 int fp8_linear_block(const void* x_bf16, const uint8_t* qw, const float* sw,
                      void* y_bf16, int64_t M, int64_t N, int64_t K,
                      uint8_t* qx_out, float* sx_out, uint32_t flags, void* ws,

@@ -69,4 +69,11 @@ void launch_calib_scale(const void* x, int64_t n, int64_t k_lo, int64_t k_hi,
 void launch_quant_static(const void* x, int64_t n, const float* scale, uint8_t* q,
                          hipStream_t st);
 
+// Static device scratch of the no-allocation entry point (noalloc.hip):
+// this device's copy of the array (its address from hipGetSymbolAddress,
+// taken once per device) and its size; nullptr if the address could not be
+// obtained.
+constexpr size_t kScratchBytes = kDecodeCounterBytes + ((size_t)16 << 20);
+void* scratch_for_current_device();
+
 }  // namespace fp8dq

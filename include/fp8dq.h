@@ -184,6 +184,25 @@ int fp8_linear(const void* x_bf16, const uint8_t* qw, const float* sw,
                size_t ws_bytes, void* stream);
 
 /*
+ * fp8_linear_noalloc -- fp8_linear for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same computation with no workspace argument. The
+ * decode path's split-K partials and tile counters live in a static device
+ * array of the library, FP8DQ_NOALLOC_SCRATCH_BYTES per GPU (16 MiB + 16
+ * KiB, held from the first call on a GPU until the process ends), and the
+ * decode plans only split K as far as that array holds; the result is within
+ * the tolerance of fp8_linear's (bit-identical where fp8_linear's plan fits
+ * the array). The call allocates nothing. All calls on one GPU share its
+ * array: calls that overlap on one GPU (several streams or threads) race.
+ * Arguments, size rules and errors: those of fp8_linear; FP8DQ_ERR_HIP if
+ * the array's device address cannot be obtained.
+ */
+#define FP8DQ_NOALLOC_SCRATCH_BYTES ((size_t)16 * 1024 * 1024 + 16 * 1024)
+int fp8_linear_noalloc(const void* x_bf16, const uint8_t* qw, const float* sw,
+                       void* y_bf16, int64_t M, int64_t N, int64_t K,
+                       uint8_t* qx_out, float* sx_out, uint32_t flags, void* stream);
+
+/*
  * fp8_linear_block -- block variant: quantize X per token per 128-group
  * (qx_out uint8 [M, K], sx_out fp32 [M, K/128]) then fp8_gemm_block with
  * block-quantized weights (qw, sw from fp8_quant_weight_block).
