@@ -61,9 +61,10 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 //    is exactly one scale group g, whose 256 activation
 //    scales ride with the pair into a per-slot LDS ring, and the tile's
 //    weight-block scales for every g are loaded once. One accumulator carries
-//    the sum in units of the current factor f_g = sx[m,g] * sw[nb,g]: it is
-//    multiplied by f_{g-1} / f_g before group g's first MFMAs (a zero factor,
-//    an all-zero group, leaves it alone) and by the last factor at the end.
+//    the sum in units of the current factor f_g = sx[m,g] * sw[nb,g] (held
+//    above 2^-64 of the largest factor so far and above 2^-126, so it never
+//    overflows): it is multiplied by u_{g-1} / u_g before group g's first
+//    MFMAs and by the last units at the end.
 //    The next group's scales are read right after the odd step's barrier and
 //    its factor is formed a few MFMAs later, so the matrix core does not
 //    wait for those reads.
@@ -267,11 +268,11 @@ __global__ __launch_bounds__((64 * LineCfg<BLOCK, BNP>::NW), 1) void gemm_prefil
   };
 
   v16f acc[DNI][DMJ];
-  // block: factor the accumulator is counted in, per row j, and the rescale
-  // for the next group (formed one step ahead)
-  float fcur[DMJ], fnext[DMJ], rho[DMJ];
+  // block: factor the accumulator is counted in, per row j, the largest
+  // factor so far, and the rescale for the next group (formed one step ahead)
+  float fcur[DMJ], fmax[DMJ], rho[DMJ];
 #pragma unroll
-  for (int j = 0; j < DMJ; ++j) { fcur[j] = 0.f; fnext[j] = 0.f; rho[j] = 1.f; }
+  for (int j = 0; j < DMJ; ++j) { fcur[j] = 0.f; fmax[j] = 0.f; rho[j] = 1.f; }
   // group g's scales of this lane's rows, read from LDS (gsx, gsw) ...
   float gsx[DMJ], gsw = 0.f;
   auto group_scales = [&](int g, int si) {
@@ -284,14 +285,24 @@ __global__ __launch_bounds__((64 * LineCfg<BLOCK, BNP>::NW), 1) void gemm_prefil
 #pragma unroll
     for (int j = 0; j < DMJ; ++j) gsx[j] = sxs[wm * DTM + 32 * j + lr];
   };
-  // ... and f_g -> rho, fnext (formed later, so the reads' latency is hidden)
+  // ... and f_g -> rho and the next units (formed later, so the reads'
+  // latency is hidden). The accumulator counts in units
+  //   u_g = max(f_g, 2^-64 * (largest factor so far), 2^-126):
+  // the ratio u_{g-1} / u_g then stays below 2^65 and rcp never sees a
+  // subnormal, so the carried sum stays below 2^98 whatever the scales
+  // (zero groups, factors below the fp32 range, drops of any size). A group
+  // whose factor lies below the floor is weighted by u_g instead of f_g; its
+  // share of y then errs by at most 2^24 * 2^-64 of the largest factor, far
+  // below the fp32 rounding of the largest group's own share. gsx[j] is
+  // replaced by u_g.
   auto group_factor = [&]() {
 #pragma unroll
     for (int j = 0; j < DMJ; ++j) {
       const float f = gsx[j] * gsw;
-      const bool live = f != 0.0f;
-      rho[j] = live ? fcur[j] * __builtin_amdgcn_rcpf(f) : 1.0f;
-      fnext[j] = live ? f : fcur[j];
+      fmax[j] = __builtin_fmaxf(fmax[j], f);
+      const float u = __builtin_fmaxf(__builtin_fmaxf(f, fmax[j] * 0x1p-64f), 0x1p-126f);
+      rho[j] = fcur[j] * __builtin_amdgcn_rcpf(u);
+      gsx[j] = u;
     }
   };
 
@@ -320,11 +331,11 @@ __global__ __launch_bounds__((64 * LineCfg<BLOCK, BNP>::NW), 1) void gemm_prefil
     for (int r = 0; r < NR; ++r) read_frag(oA, oB, A[0], B[0], cs, 0, frag_of(r >> 1), r & 1);
     if constexpr (BLOCK) {
 #pragma unroll
-      for (int j = 0; j < DMJ; ++j) { fcur[j] = 0.f; rho[j] = 1.f; }
+      for (int j = 0; j < DMJ; ++j) { fcur[j] = 0.f; fmax[j] = 0.f; rho[j] = 1.f; }
       group_scales(0, cs);
       group_factor();
 #pragma unroll
-      for (int j = 0; j < DMJ; ++j) fcur[j] = fnext[j];   // rho of group 0 is unused
+      for (int j = 0; j < DMJ; ++j) fcur[j] = gsx[j];   // rho of group 0 is unused
     }
   };
   prologue(0);
@@ -433,8 +444,10 @@ __global__ __launch_bounds__((64 * LineCfg<BLOCK, BNP>::NW), 1) void gemm_prefil
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (BLOCK && cur == 1) {
+      if (more) {
 #pragma unroll
-      for (int j = 0; j < DMJ; ++j) fcur[j] = fnext[j];
+        for (int j = 0; j < DMJ; ++j) fcur[j] = gsx[j];
+      }
     }
     if (cur == 1) cs = ns;
   };

@@ -356,38 +356,94 @@ def test_c4_block_shapes(F, j, M):
     assert_y_close(host_bf16_f64(y_d[:, torch.from_numpy(rows).cuda()]), y_ref, "y")
 
 
-def test_c5_long_context_reduced(F):
-    d = synth.workload(5, M=2048)
-    say(f"c5 M=2048 zero_rows={list(d['zero_rows'])} planted={d['planted']}")
-    x = O.bf16_to_f64(d["x"])
-    assert np.abs(x).max() > 448                       # saturation region present
-    cols = sample_idx(d["N"], 256, 55)
-    _linear_case(F, d["x"], d["w"], cols, what="c5")
+def block_ref_rows(qx, sx, qw, sw, rows, cols):
+    """Oracle y of the block variant at sampled rows and columns (float64):
+    sum over groups of the exact group product times sx[m,g] sw[n/128,g]."""
+    G = qx.shape[1] // 128
+    vx = O.e4m3_decode(qx[rows])
+    vw = O.e4m3_decode(qw[cols])
+    y = np.zeros((len(rows), len(cols)))
+    for g in range(G):
+        ks = slice(128 * g, 128 * g + 128)
+        f = sx[rows, g].astype(np.float64)[:, None] * sw[cols // 128, g].astype(np.float64)[None, :]
+        y += O.gemm_codes(qx[rows][:, ks], qw[cols][:, ks]) * f
+    return y
 
 
-# ----------------------------------------------------------------------------
-# Full-size runs in the launch configuration the benchmark times
-# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,flags", [(8192, 8192, 1), (512, 512, 1), (64, 512, 1), (48, 512, 2)],
+                         ids=["wide_tiles", "narrow_tiles", "narrow_m64", "decode"])
+def test_block_factor_extremes(F, M, N, flags):
+    """Block factors sx * sw spanning the fp32 range, made by multiplying a
+    row's own group scales (so y stays of order 1, as in real data): later
+    groups 2^90 and 2^120 below the first (the largest carried ratio of a
+    single accumulator would overflow fp32 at 2^120), the first group 2^120
+    below the rest, two activation scales in the fp32 subnormals (1e-41,
+    whose product with a weight scale of 2e-4 is subnormal; 1e-42, whose
+    product underflows to 0), factors rising by 2^10 and falling by 2^12 per
+    group, and unchanged rows. Codes are those of the synthetic activations;
+    y within tolerance of the oracle on sampled rows and columns (8192 x 8192
+    runs the 256 x 256 whole-line tiles, 512 x 512 the 256 x 128 ones)."""
+    K = 1024
+    G = K // 128
+    say(f"block factor extremes {M}x{N} flags={flags}")
+    qx, sx = O.quant_per_group(synth.activations(M, K, 3100 + M, 3200))
+    qw, sw = O.quant_weight_block(synth.weights(N, K, 3300 + N))
+    g = np.arange(G)
+    mult = {
+        0: np.where(g >= 1, 2.0 ** -90, 1.0),      # later groups 2^90 below
+        1: np.where(g >= 1, 2.0 ** -120, 1.0),     # 2^120 below
+        2: np.where(g == 0, 2.0 ** -120, 1.0),     # the first group 2^120 below
+        4: 2.0 ** (10.0 * g - 70),                 # rising by 2^10
+        5: 2.0 ** (-12.0 * g),                     # falling by 2^12
+    }
+    sx = sx.copy()
+    for r in range(M):
+        k = r % 8
+        if k in mult:
+            sx[r] = (sx[r].astype(np.float64) * mult[k]).astype(np.float32)
+        elif k == 3:   # a zero factor right after a normal one, then a subnormal one
+            sx[r, 3], sx[r, 5] = np.float32(1e-42), np.float32(1e-41)
+    sw = sw.copy()
+    sw[:, 3] = sw[:, 5] = np.float32(2e-4)                          # with the subnormal sx
+    # fp32 products: 1e-41 * 2e-4 is subnormal, 1e-42 * 2e-4 underflows to 0
+    assert 0 < np.float32(1e-41) * np.float32(2e-4) < 2.0 ** -126
+    assert np.float32(1e-42) * np.float32(2e-4) == 0
+    y = F.fp8_gemm_block(dev(qx), dev(sx), dev(qw), dev(sw), flags=flags)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(16), sample_idx(M, 48, 31)]))
+    cols = np.unique(np.concatenate([np.arange(8), sample_idx(N, 40, 32)]))
+    ref = block_ref_rows(qx, sx, qw, sw, rows, cols)
+    got = host_bf16_f64(y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
+    assert np.all(np.isfinite(got)), "non-finite outputs"
+    assert_y_close(got, ref, "y")
+
+
 @pytest.mark.parametrize("j", [0, 1, 2, 3])
-def test_c2_full_size_sampled(F, j):
-    d = synth.workload(2, j)
-    M, N = d["M"], d["N"]
-    say(f"c2 full {d['name']} {M}x{d['K']}->{N}")
-    rows = sample_idx(M, 48, 70 + j)
-    cols = sample_idx(N, 96, 80 + j)
+def test_c4_full_size_sampled(F, j):
+    """The Llama-3.2-3B block linears at M = 8192 through fp8_linear_block,
+    in the launch configuration the benchmark times (256 x 256 whole-line
+    tiles for gate_up, walking several tiles per workgroup; the wide-then-
+    narrow column split for the others): codes and scales of sampled rows
+    and weight blocks bit-exact, y within tolerance there."""
+    d = synth.workload(4, j)
+    M, N, K = d["M"], d["N"], d["K"]
+    say(f"c4 full {d['name']} {M}x{K}->{N}")
+    rows = sample_idx(M, 48, 90 + j)
+    bands = np.unique([0, 1, N // 256, N // 128 - 2, N // 128 - 1])
+    cols = np.concatenate([np.arange(b * 128, b * 128 + 128) for b in bands])
     x_d = dev_bf16(d["x"])
     w_d = dev_bf16(d["w"])
-    qw_d, sw_d = F.fp8_quant_act(w_d)
-    y_d, qx_d, sx_d = F.fp8_linear(x_d, qw_d, sw_d)
+    qw_d, sw_d = F.fp8_quant_weight_block(w_d)
+    y_d, qx_d, sx_d = F.fp8_linear_block(x_d, qw_d, sw_d)
     torch.cuda.synchronize()
-    qw_o, sw_o = O.quant_per_row(d["w"][cols])
-    qx_o, sx_o = O.quant_per_row(d["x"][rows])
+    qw_o, sw_o = O.quant_weight_block(d["w"][cols])
+    qx_o, sx_o = O.quant_per_group(d["x"][rows])
     assert_codes_equal(qw_d.cpu().numpy()[cols], qw_o, "weight codes")
-    assert_scales_equal(sw_d.cpu().numpy()[cols], sw_o, "weight scales")
+    assert_scales_equal(sw_d.cpu().numpy()[bands], sw_o, "weight block scales")
     assert_codes_equal(qx_d.cpu().numpy()[rows], qx_o, "act codes")
     assert_scales_equal(sx_d.cpu().numpy()[rows], sx_o, "act scales")
     ysub = y_d[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()]
-    assert_y_close(host_bf16_f64(ysub), O.linear_per_channel(qx_o, sx_o, qw_o, sw_o), "y")
+    assert_y_close(host_bf16_f64(ysub), O.linear_block(qx_o, sx_o, qw_o, sw_o), "y")
 
 
 def test_c5_full_size_sampled(F):
