@@ -28,8 +28,23 @@ Also reported:
 Other modes (profiling helpers, no JSON line):
   --copy-calibration        a plain 1 GiB device copy, three times, for
                             scaling the FETCH_SIZE / WRITE_SIZE counters;
-  --summarize-profile DIR   per-kernel, per-grid duration / counter summary
-                            of a rocprofv3 csv output directory.
+  --profile-case CASE --profile-out DIR
+                            one labelled workload for a rocprofv3 run (its
+                            kernels and their algorithmic bytes per launch
+                            go to DIR/case.json); CASE is one of
+                              copy                  the 1 GiB copy, 3 times
+                              decode:LINEAR:M       fp8_linear, 70B LINEAR at
+                                                    M tokens, cold weights
+                              quant:M:K             per-token quantizer, cold
+                              prefill:LINEAR        8B prefill GEMM (codes in)
+                              block:LINEAR          3B block GEMM (codes in);
+  --summarize-profile DIR [DIR ...]
+                            per-kernel, per-grid duration / counter summary
+                            of rocprofv3 csv output directories; with
+                            --profile-case directories, per case and kernel:
+                            counter bytes (scaled by the copy case's) against
+                            algorithmic bytes, clock and matrix-core busy
+                            share, wave-state shares.
 """
 import argparse
 import csv
@@ -462,33 +477,274 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
 
 
-def summarize_profile(d):
-    """Print per-kernel, per-grid-size averages of a rocprofv3 csv directory
-    (kernel trace and/or counter collection)."""
-    rows = []
+PROFILE_REPS = {"copy": (0, 3), "decode": (4, 8), "quant": (4, 8), "prefill": (2, 4),
+                "block": (2, 4)}
+
+
+def profile_case(case, out_dir, torch):
+    """Run one labelled workload; write out_dir/case.json with the kernels it
+    launches (name prefixes) and their algorithmic bytes and flops per launch."""
+    import synth
+    import fp8_dynamic_quantized_amd as F
+    kind = case.split(":")[0]
+    warm, reps = PROFILE_REPS[kind]
+    kernels = []
+    if kind == "copy":
+        src = torch.randint(0, 255, (COPY_BYTES,), dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        run = lambda i: dst.copy_(src)                      # noqa: E731
+        kernels.append({"match": "copyBuffer", "bytes": 2 * COPY_BYTES, "flops": 0,
+                        "read": COPY_BYTES, "write": COPY_BYTES, "what": "1 GiB device copy"})
+    elif kind == "decode":
+        _, lin, ms = case.split(":")
+        M = int(ms)
+        j = [n for n, _, _ in synth.SHAPES["c3"]].index(lin)
+        _, K, N = synth.SHAPES["c3"][j]
+        w = to_dev(synth.workload(3, j, x=False)["w"], torch)
+        qw, sw = F.fp8_quant_act(w)
+        del w
+        copies = max(2, -(-(2 << 30) // (N * K)) + 1)
+        qws = [qw] + [qw.clone() for _ in range(copies - 1)]
+        x = to_dev(synth.activations(M, K, 7 + M, 8 + K), torch)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        qx = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+        sxv = torch.empty((M,), dtype=torch.float32, device="cuda")
+        ws = torch.zeros(max(16, F.fp8_workspace_bytes(M, N, K)), dtype=torch.uint8,
+                         device="cuda")
+        run = lambda i: F.fp8_linear(x, qws[i % copies], sw, y=y, qx_out=qx,   # noqa: E731
+                                     sx_out=sxv, ws=ws)
+        rd = N * K + 4 * N + M * K + 4 * M
+        kernels.append({"match": "gemm_decode", "bytes": rd + 2 * M * N, "read": rd,
+                        "write": 2 * M * N, "flops": 2 * M * N * K,
+                        "what": f"70B {lin} {K}->{N} at M={M}: weights N*K + 4N, codes M*K + 4M, y 2MN"})
+        kernels.append({"match": "quant_rows", "bytes": 3 * M * K + 4 * M, "read": 2 * M * K,
+                        "write": M * K + 4 * M, "flops": 0,
+                        "what": f"per-token quantizer {M}x{K}: x 2MK, codes MK, scales 4M"})
+    elif kind == "quant":
+        _, ms, ks = case.split(":")
+        M, K = int(ms), int(ks)
+        copies = max(2, -(-(1 << 30) // (2 * M * K)) + 1)
+        xs = [to_dev(synth.activations(M, K, 9 + c, 10), torch) for c in range(min(copies, 3))]
+        xs += [xs[c % 3].clone() for c in range(3, copies)]
+        q = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((M,), dtype=torch.float32, device="cuda")
+        run = lambda i: F.fp8_quant_act(xs[i % copies], q=q, scale=sc)   # noqa: E731
+        kernels.append({"match": "quant_rows", "bytes": 3 * M * K + 4 * M, "read": 2 * M * K,
+                        "write": M * K + 4 * M, "flops": 0,
+                        "what": f"per-token quantizer {M}x{K} read cold: x 2MK, codes MK, scales 4M"})
+    elif kind in ("prefill", "block"):
+        _, lin = case.split(":")
+        c = 2 if kind == "prefill" else 4
+        j = [n for n, _, _ in synth.SHAPES[f"c{c}"]].index(lin)
+        _, K, N = synth.SHAPES[f"c{c}"][j]
+        M = synth.M_OF[f"c{c}"][0]
+        d = synth.workload(c, j)
+        x, w = to_dev(d["x"], torch), to_dev(d["w"], torch)
+        if kind == "prefill":
+            qx, sxv = F.fp8_quant_act(x)
+            qw, sw = F.fp8_quant_act(w)
+            run = lambda i: F.fp8_gemm(qx, sxv, qw, sw)     # noqa: E731
+            sbytes = 4 * (M + N)
+            match = "gemm_prefill_line_kernel<false"
+        else:
+            qx, sxv = F.fp8_quant_act(x, group=128)
+            qw, sw = F.fp8_quant_weight_block(w)
+            run = lambda i: F.fp8_gemm_block(qx, sxv, qw, sw)   # noqa: E731
+            sbytes = 4 * (M * K // 128 + (N // 128) * (K // 128))
+            match = "gemm_prefill_line_kernel<true"
+        del x, w
+        rd = M * K + N * K + sbytes
+        kernels.append({"match": match, "bytes": rd + 2 * M * N, "read": rd,
+                        "write": 2 * M * N, "flops": 2 * M * N * K,
+                        "what": f"{'8B' if c == 2 else '3B block'} {lin} M={M} {K}->{N}: "
+                                f"codes MK + NK, scales, y 2MN"})
+    else:
+        raise SystemExit(f"unknown profile case {case}")
+    for i in range(warm):
+        run(i)
+    torch.cuda.synchronize()
+    for i in range(reps):
+        run(warm + i)
+    torch.cuda.synchronize()
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "case.json"), "w") as f:
+        json.dump({"case": case, "warmup": warm, "launches": reps, "kernels": kernels}, f)
+    log(f"profile case {case}: {warm} + {reps} launches")
+
+
+def _read_profile_dir(d):
+    """(case dict or None, {dispatch_id: (kernel, grid, ns)}, {dispatch_id: {counter: v}})"""
+    case = None
+    cj = os.path.join(d, "case.json")
+    if os.path.exists(cj):
+        with open(cj) as f:
+            case = json.load(f)
+    trace = {}
     for p in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
         with open(p) as f:
             for r in csv.DictReader(f):
-                rows.append((r["Kernel_Name"], int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"])
-                             * int(r["Grid_Size_Z"]),
-                             int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
-    if rows:
-        agg = {}
-        for name, grid, ns in rows:
-            agg.setdefault((name, grid), []).append(ns)
-        print(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'grid':>10}  kernel")
-        for (name, grid), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
-            print(f"{len(v):6d} {np.mean(v) / 1e3:10.2f} {min(v) / 1e3:10.2f} "
-                  f"{max(v) / 1e3:10.2f} {grid:10d}  {name[:110]}")
+                grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+                trace[int(r["Dispatch_Id"])] = (r["Kernel_Name"], grid,
+                                                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    ctr = {}
+    names = {}
     for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-        agg = {}
         with open(p) as f:
             for r in csv.DictReader(f):
-                key = (r["Kernel_Name"], int(r["Grid_Size"]), r["Counter_Name"])
-                agg.setdefault(key, []).append(float(r["Counter_Value"]))
-        print(f"{'calls':>6} {'avg':>14} {'grid':>10} {'counter':>12}  kernel")
-        for (name, grid, cn), v in sorted(agg.items()):
-            print(f"{len(v):6d} {np.mean(v):14.2f} {grid:10d} {cn:>12}  {name[:110]}")
+                did = int(r["Dispatch_Id"])
+                ctr.setdefault(did, {})[r["Counter_Name"]] = \
+                    ctr.get(did, {}).get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                names[did] = (r["Kernel_Name"], int(r["Grid_Size"]))
+    return case, trace, ctr, names
+
+
+def summarize_profile(dirs):
+    """Per-kernel, per-grid averages of rocprofv3 csv directories; for
+    --profile-case directories, the per-case table of counter bytes against
+    algorithmic bytes (and clock / matrix-core / wave-state shares)."""
+    cases = {}
+    for d in dirs:
+        case, trace, ctr, names = _read_profile_dir(d)
+        if case is None:
+            # plain directory: per kernel and grid
+            agg = {}
+            for name, grid, ns in trace.values():
+                agg.setdefault((name, grid), []).append(ns)
+            print(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'grid':>10}  kernel")
+            for (name, grid), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+                print(f"{len(v):6d} {np.mean(v) / 1e3:10.2f} {min(v) / 1e3:10.2f} "
+                      f"{max(v) / 1e3:10.2f} {grid:10d}  {name[:110]}")
+            # the prefill step of this benchmark launches, per step, the qkv
+            # GEMM (256 x 192 tiles) and then o, gate_up and down (256 x 256
+            # tiles, the same grid): the gate_up launches are the middle ones
+            seq = [trace[k] for k in sorted(trace)]
+            n_qkv = sum(1 for nm, _, _ in seq if "gemm_prefill_line_kernel<false, 192>" in nm)
+            wide = [ns for nm, _, ns in seq if DOM_KERNEL in nm][: 3 * n_qkv]
+            if n_qkv and len(wide) == 3 * n_qkv:
+                gu = [ns / 1e3 for ns in wide[1::3]]
+                print(f"# gate_up GEMM launches of the prefill steps ({len(gu)}, warm-up "
+                      f"first): " + " ".join(f"{v:.1f}" for v in gu))
+                for last in (20, 10):
+                    if len(gu) >= last:
+                        print(f"# gate_up GEMM, mean of the last {last} launches: "
+                              f"{np.mean(gu[-last:]):.2f} us")
+            cagg = {}
+            for did, cv in ctr.items():
+                for cn, v in cv.items():
+                    cagg.setdefault((names[did][0], names[did][1], cn), []).append(v)
+            if cagg:
+                print(f"{'calls':>6} {'avg':>16} {'grid':>10} {'counter':>24}  kernel")
+                for (name, grid, cn), v in sorted(cagg.items()):
+                    print(f"{len(v):6d} {np.mean(v):16.2f} {grid:10d} {cn:>24}  {name[:110]}")
+            continue
+        ent = cases.setdefault(case["case"], {"case": case, "disp": {}})
+        if not ctr:      # a kernel-trace run: the durations
+            for did, (name, grid, ns) in trace.items():
+                ent["disp"][("t", d, did)] = {"name": name, "grid": grid, "ns": ns, "ctr": {},
+                                              "trace_run": True}
+        for did, cv in ctr.items():
+            ent["disp"][("c", d, did)] = {"name": names[did][0], "grid": names[did][1],
+                                          "ns": trace[did][2] if did in trace else None,
+                                          "ctr": dict(cv), "trace_run": False}
+    if not cases:
+        return
+    # counter scaling from the copy case: known bytes / counter bytes
+    scale = {"FETCH_SIZE": None, "WRITE_SIZE": None}
+    if "copy" in cases:
+        for cn in scale:
+            v = [e["ctr"][cn] for e in cases["copy"]["disp"].values()
+                 if cn in e["ctr"] and "copyBuffer" in e["name"]]
+            if v:
+                scale[cn] = COPY_BYTES / (float(np.mean(v)) * 1024.0)
+        print(f"# counter scale factors (1 GiB copy: bytes / counter KiB x 1024): "
+              f"FETCH_SIZE {scale['FETCH_SIZE']}, WRITE_SIZE {scale['WRITE_SIZE']}")
+    for cname, ent in cases.items():
+        if cname == "copy":
+            continue
+        case = ent["case"]
+        print(f"\n## case {cname} ({case['launches']} timed launches after {case['warmup']})")
+        for k in case["kernels"]:
+            es = [e for e in ent["disp"].values() if k["match"] in e["name"]]
+            if not es:
+                print(f"  {k['match']}: no dispatches")
+                continue
+            # kernels launched once per run (set-up, e.g. the weight
+            # quantization before a decode case) are left out
+            per_run = case["warmup"] + case["launches"]
+            runs = len({key[1] for key, e in ent["disp"].items()})
+            names = sorted({e["name"] for e in es})
+            for nm in names:
+                ee = [e for e in es if e["name"] == nm]
+                if len(ee) < per_run * max(1, runs) // 2:
+                    continue
+                tr = [e for e in ee if e["trace_run"]]
+                dur = [e["ns"] / 1e3 for e in (tr or ee) if e["ns"] is not None]
+                line = [f"  {nm[:100]}", f"    {k['what']}"]
+                avg_us = float(np.median(dur)) if dur else None
+                if avg_us:
+                    line.append(f"    dispatches {len(ee)}, median duration {avg_us:.2f} us "
+                                f"(min {min(dur):.2f}, max {max(dur):.2f})")
+                alg = k["bytes"]
+                line.append(f"    algorithmic: read {k['read'] / 1e6:.3f} MB, write "
+                            f"{k['write'] / 1e6:.3f} MB, total {alg / 1e6:.3f} MB"
+                            + (f", {k['flops'] / 1e9:.2f} GFLOP" if k["flops"] else ""))
+                if avg_us:
+                    line.append(f"    algorithmic rate {alg / avg_us / 1e3:.0f} GB/s "
+                                f"({alg / avg_us / 1e3 / PEAK_HBM_GBS * 100:.1f} % of 8 TB/s)"
+                                + (f", {k['flops'] / avg_us / 1e6:.0f} TFLOP/s "
+                                   f"({k['flops'] / avg_us / 1e6 / PEAK_FP8_TFLOPS * 100:.1f} % of 5 PF)"
+                                   if k["flops"] else ""))
+                meas = {}
+                for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+                    v = [e["ctr"][cn] for e in ee if cn in e["ctr"]]
+                    if v and scale[cn]:
+                        meas[cn] = float(np.mean(v)) * 1024.0 * scale[cn]
+                if meas:
+                    rd = meas.get("FETCH_SIZE")
+                    wr = meas.get("WRITE_SIZE")
+                    parts = []
+                    if rd is not None:
+                        parts.append(f"read {rd / 1e6:.3f} MB ({rd / k['read']:.2f}x)")
+                    if wr is not None:
+                        parts.append(f"write {wr / 1e6:.3f} MB ({wr / max(k['write'], 1):.2f}x)")
+                    if rd is not None and wr is not None:
+                        parts.append(f"total {(rd + wr) / 1e6:.3f} MB ({(rd + wr) / alg:.2f}x)")
+                        if avg_us:
+                            parts.append(f"{(rd + wr) / avg_us / 1e3:.0f} GB/s measured")
+                    line.append("    counters (scaled): " + ", ".join(parts))
+                g = [e["ctr"] for e in ee if "GRBM_GUI_ACTIVE" in e["ctr"]]
+                if g and avg_us:
+                    ga = float(np.mean([c["GRBM_GUI_ACTIVE"] for c in g]))
+                    clk = ga / 8.0 / (avg_us * 1e3)        # 8 XCDs, GHz
+                    line.append(f"    clock {clk:.2f} GHz (GRBM_GUI_ACTIVE / 8 XCDs / duration)")
+                    mb = [c["SQ_VALU_MFMA_BUSY_CYCLES"] for c in g if "SQ_VALU_MFMA_BUSY_CYCLES" in c]
+                    if mb:
+                        per_simd = float(np.mean(mb)) / 1024.0
+                        line.append(f"    matrix cores busy {per_simd / (ga / 8.0) * 100:.1f} % "
+                                    f"(SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / busy cycles)")
+                w = [e["ctr"] for e in ee if "SQ_WAVE_CYCLES" in e["ctr"]]
+                if w:
+                    wc = float(np.mean([c["SQ_WAVE_CYCLES"] for c in w]))
+                    shares = []
+                    for cn, lab in (("SQ_WAIT_ANY", "waiting (s_waitcnt and other waits)"),
+                                    ("SQ_WAIT_INST_ANY", "ready instruction not issued"),
+                                    ("SQ_ACTIVE_INST_VALU", "issuing VALU"),
+                                    ("SQ_ACTIVE_INST_LDS", "issuing LDS")):
+                        v = [c[cn] for c in w if cn in c]
+                        if v and wc > 0:
+                            shares.append(f"{lab} {float(np.mean(v)) / wc * 100:.1f} %")
+                    lds = [c["SQ_LDS_BANK_CONFLICT"] for c in w if "SQ_LDS_BANK_CONFLICT" in c]
+                    if lds:
+                        shares.append(f"SQ_LDS_BANK_CONFLICT {float(np.mean(lds)):.0f}")
+                    line.append("    wave time (SQ_*/SQ_WAVE_CYCLES): " + ", ".join(shares))
+                print("\n".join(line))
+                if DOM_KERNEL in nm and "FETCH_SIZE" in meas and "WRITE_SIZE" in meas:
+                    # the lines bench.py reads back for the roofline's traffic
+                    print(f"kernel: {DOM_KERNEL}")
+                    print(f"kernel_source_sha256: {kernel_source_hash()}")
+                    print(f"fetch_bytes_per_launch: {meas['FETCH_SIZE']:.0f}")
+                    print(f"write_bytes_per_launch: {meas['WRITE_SIZE']:.0f}")
+                    print(f"traffic_bytes_per_launch: {meas['FETCH_SIZE'] + meas['WRITE_SIZE']:.0f}")
 
 
 def main():
@@ -515,7 +771,9 @@ def main():
                          "the gate_up launches apart: every per-channel linear "
                          "of this size launches the same grid); must include gate_up")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--summarize-profile", metavar="DIR")
+    ap.add_argument("--summarize-profile", metavar="DIR", nargs="+")
+    ap.add_argument("--profile-case", metavar="CASE")
+    ap.add_argument("--profile-out", metavar="DIR")
     args = ap.parse_args()
 
     if args.summarize_profile:
@@ -533,6 +791,12 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.profile_case:
+        from fp8_dynamic_quantized_amd import build as B
+        if not os.path.exists(B.LIB):
+            B.build()
+        profile_case(args.profile_case, args.profile_out or ".", torch)
         return
 
     import fp8_dynamic_quantized_amd as F
