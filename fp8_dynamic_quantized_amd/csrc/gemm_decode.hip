@@ -8,15 +8,19 @@
 // comes from moving half the bytes).
 //
 // Two kernels, by token count:
-//  * up to 16 rows, gemm_decode_kernel: a workgroup owns 16 weight rows and
+//  * up to 8 rows, gemm_decode_kernel: a workgroup owns 16 weight rows and
 //    one K slice; its 4 waves take interleaved 128-byte K steps with a 4-deep
 //    register prefetch of weight and token-row fragments (plain 16-byte
 //    loads, bounded only by registers), and add their partial sums in a
 //    fixed order through LDS;
-//  * 17-64 rows, gemm_decode_line_kernel: 128 weight rows per workgroup (32
+//  * 9-64 rows, gemm_decode_line_kernel: 128 weight rows per workgroup (32
 //    per wave); weights and the token rows' codes move L2 -> LDS with
 //    whole-line loads into a 3-slot ring, the token rows loaded once per
-//    workgroup and shared by its waves.
+//    workgroup and shared by its waves. Every token row then costs 1/128 of
+//    the weight bytes, against 1/16 in the register kernel, whose token-row
+//    loads took 30-37 % of its time at 16 rows on the 70B linears. Each
+//    workgroup starts its K slice at its own pair (a rotation by 7 pairs per
+//    workgroup index) and wraps around.
 //
 // Accuracy. The FP8 matrix instruction adds its products in groups of 8
 // consecutive K; inside a group every product is cut (toward zero) to a
@@ -128,7 +132,7 @@ __device__ __forceinline__ void store_out(uint16_t* __restrict__ y, const float*
 }
 
 // ---------------------------------------------------------------------------
-// Register-loading kernel (up to 16 token rows).
+// Register-loading kernel (up to 8 token rows).
 // ---------------------------------------------------------------------------
 template <bool BLOCK>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(
@@ -149,7 +153,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
 
   // MFMA operand A: 16 weight rows; B: 16 token rows. Lanes of padding token
   // rows (lr >= M) get an offset past the buffer and load nothing; their
-  // outputs are dropped. M * K < 2^31 on this path (M <= 16, K <= 2^17).
+  // outputs are dropped. M * K < 2^31 on this path (M <= 8, K <= 2^17).
   const __amdgpu_buffer_rsrc_t xrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)qx, (short)0, M * K, 0x00020000);
   const uint8_t* wp = qw + (int64_t)min(n0 + lr, N - 1) * K + kg * 32;
@@ -196,6 +200,20 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
   // compiler cannot count loads across the tail's conditions and waits for
   // all of them there, draining the D steps in flight).
   int t0 = 0;
+  if (cntw >= D && cntw % D == 0) {
+    // whole batches: the last one loads nothing, so its waits stay exact
+    const int nb = cntw / D;
+    for (int bt = 0; bt + 1 < nb; ++bt) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        compute(d);
+        load(d, (bt + 1) * D + d);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) compute(d);
+    t0 = cntw;
+  }
   for (; t0 + 2 * D <= cntw; t0 += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -335,8 +353,16 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_line_kernel(
       ? (wave == 1 ? (uint32_t)(n0 >> 7) * (uint32_t)KP * 4u
                    : (uint32_t)min(lane, M - 1) * (uint32_t)KP * 4u)
       : 0u;
+  // Pair p of the slice is its pair (p + rot) mod np. Workgroups that start
+  // together on the same K offset read their 128 rows at addresses a
+  // multiple of K apart at the same moment; spreading the starting offsets
+  // over the slice measured 3-16 % faster on the 70B linears at 16-64
+  // tokens (the multiplier 7 was the best of 1, 7 and 29 at 64 tokens).
+  const int rot = (int)((blockIdx.x * 7u) % (unsigned)np);
   auto issue = [&](int p) {   // pair p of this slice (clamped) into slot p % DL_NSL
-    const int pc = p0 + min(p, np - 1);
+    int pq = min(p, np - 1) + rot;
+    pq -= pq >= np ? np : 0;
+    const int pc = p0 + pq;
     const uint32_t sb = lds0 + (uint32_t)((p % DL_NSL) * SLOT);
     const size_t koff = (size_t)pc * BK;
 #pragma unroll
@@ -524,9 +550,12 @@ DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, size_t ws_cap) {
   if (p.mb < 1) p.mb = 1;
   if (p.mb > 4) p.mb = 4;  // callers guarantee M <= 64 on this path
 
-  p.line = M > 16 ? 1 : 0;
   const int64_t KT = K / BK;
   const int64_t ncu = decode_cu_count();
+  // from 9 token rows the register kernel's token-row loads cost more than
+  // the whole-line kernel's slower weight stream (70B linears at 16 rows:
+  // 3-20 % faster whole-line, except o: 8 % slower)
+  p.line = M > 8 ? 1 : 0;
   if (p.line) {
     // Whole-line kernel: 128 weight rows per workgroup, two workgroups per
     // CU. Split K until there are >= 1.5 workgroups per CU, keeping at least
@@ -589,6 +618,8 @@ void launch_gemm_decode(const uint8_t* qx, const float* sx, const uint8_t* qw,
     return;
   }
   switch (p.mb) {
+    case 1: block ? launch_line_dec<1, true>(qx, sx, qw, sw, y, part, cnt, M, N, K, p, st)
+                  : launch_line_dec<1, false>(qx, sx, qw, sw, y, part, cnt, M, N, K, p, st); break;
     case 2: block ? launch_line_dec<2, true>(qx, sx, qw, sw, y, part, cnt, M, N, K, p, st)
                   : launch_line_dec<2, false>(qx, sx, qw, sw, y, part, cnt, M, N, K, p, st); break;
     case 3: block ? launch_line_dec<3, true>(qx, sx, qw, sw, y, part, cnt, M, N, K, p, st)

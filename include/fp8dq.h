@@ -58,6 +58,9 @@
  *   - The library allocates and frees nothing, keeps no pointer after it
  *     returns and holds no mutable global state: calls are reentrant.
  *     Concurrent calls that write the same buffers race (caller's problem).
+ *     The one exception is fp8_linear_noalloc, whose static per-GPU scratch
+ *     array (and its device address, looked up once per GPU) is shared by
+ *     all its calls on that GPU.
  *   - Inputs and outputs must not overlap. Inputs must be finite (NaN / Inf
  *     are outside the contract: not checked, result unspecified).
  *   - M = 0 or N = 0 (rows = 0) is a valid empty call: FP8DQ_OK, nothing

@@ -58,7 +58,9 @@ def tile(a: np.ndarray, rows: int) -> np.ndarray:
 
 # (name, M, N, K, flags, block): which kernel runs follows from the shape
 LAW_CASES = [
-    ("decode_register", 16, 256, 512, 2, False),
+    ("decode_register", 8, 256, 512, 2, False),
+    ("decode_register_block", 8, 256, 512, 2, True),
+    ("decode_line_16_rows", 16, 4096, 512, 2, False),
     ("decode_line", 48, 256, 512, 2, False),
     ("decode_block", 48, 256, 512, 2, True),
     ("prefill_small_tile", 64, 256, 512, 1, False),

@@ -370,8 +370,9 @@ def block_ref_rows(qx, sx, qw, sw, rows, cols):
     return y
 
 
-@pytest.mark.parametrize("M,N,flags", [(8192, 8192, 1), (512, 512, 1), (64, 512, 1), (48, 512, 2)],
-                         ids=["wide_tiles", "narrow_tiles", "narrow_m64", "decode"])
+@pytest.mark.parametrize("M,N,flags", [(8192, 8192, 1), (512, 512, 1), (64, 512, 1), (48, 512, 2),
+                                       (8, 512, 2)],
+                         ids=["wide_tiles", "narrow_tiles", "narrow_m64", "decode", "decode_8_rows"])
 def test_block_factor_extremes(F, M, N, flags):
     """Block factors sx * sw spanning the fp32 range, made by multiplying a
     row's own group scales (so y stays of order 1, as in real data): later
@@ -410,7 +411,7 @@ def test_block_factor_extremes(F, M, N, flags):
     assert np.float32(1e-42) * np.float32(2e-4) == 0
     y = F.fp8_gemm_block(dev(qx), dev(sx), dev(qw), dev(sw), flags=flags)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([np.arange(16), sample_idx(M, 48, 31)]))
+    rows = np.unique(np.concatenate([np.arange(min(16, M)), sample_idx(M, 48, 31)]))
     cols = np.unique(np.concatenate([np.arange(8), sample_idx(N, 40, 32)]))
     ref = block_ref_rows(qx, sx, qw, sw, rows, cols)
     got = host_bf16_f64(y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
@@ -487,6 +488,9 @@ DECODE_CASES = [(1, 8192, 8192), (5, 100, 1664), (16, 1024, 4096), (17, 520, 320
                 (1, 8192, 28672),
                 # register kernel split on a long row at one token
                 (1, 64, 16384),
+                # whole-line kernel with one 16-row token block (9-16
+                # tokens), in 2 and 16 K slices
+                (9, 4500, 2560), (12, 4096, 16384),
                 # whole-line kernel on long rows (8, 16 and 20 K slices; more
                 # than 16 slices take the reduction's general loop)
                 (64, 8192, 28672), (40, 3000, 16384), (20, 100, 20480)]
