@@ -18,7 +18,7 @@
 //    whole-line loads into a 3-slot ring, the token rows loaded once per
 //    workgroup and shared by its waves. Every token row then costs 1/128 of
 //    the weight bytes, against 1/16 in the register kernel, whose token-row
-//    loads took 30-37 % of its time at 16 rows on the 70B linears. Each
+//    loads added 14-37 % to its time at 16 rows on the 70B linears. Each
 //    workgroup starts its K slice at its own pair (a rotation by 7 pairs per
 //    workgroup index) and wraps around.
 //
@@ -552,9 +552,9 @@ DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, size_t ws_cap) {
 
   const int64_t KT = K / BK;
   const int64_t ncu = decode_cu_count();
-  // from 9 token rows the register kernel's token-row loads cost more than
-  // the whole-line kernel's slower weight stream (70B linears at 16 rows:
-  // 3-20 % faster whole-line, except o: 8 % slower)
+  // above 8 token rows, the whole-line kernel: on the 70B linears it was
+  // 11-20 % faster than the register kernel at 16 rows (o 8 % slower) and
+  // slower at 8 (the register kernel's token-row loads grow with the rows)
   p.line = M > 8 ? 1 : 0;
   if (p.line) {
     // Whole-line kernel: 128 weight rows per workgroup, two workgroups per

@@ -26,8 +26,12 @@
  *   y     = bf16_RNE( sum_k val(qx[m,k]) val(qw[n,k]) * sx[m] * sw[n] )
  *   block: y = bf16_RNE( sum_g (sum_{k in g} val*val) * sx[m,g] * sw[n/128,g] )
  *   The sum is accumulated in fp32 (any order); codes and scales are
- *   bit-exact, y is within 1e-2 relative / 1e-3 absolute of the exact value
- *   on the workloads the tests cover (see "Accumulation" below).
+ *   bit-exact. y is within 1e-2 relative / 1e-3 absolute of the exact value
+ *   on the decode path; the prefill path is exact to the matrix
+ *   instruction's own accumulation (below), which leaves rare outputs near
+ *   zero outside that tolerance (8 of 16.8 M outputs of the Llama-3.1-8B
+ *   down linear at 4096 tokens, 1 of 940 M of its gate_up at 32768 tokens,
+ *   by at most 1.5 times the allowed error).
  *
  * Accumulation (measured on gfx950, both FP8 MFMA shapes): the matrix
  * instruction adds its products in groups of 8 consecutive k. Inside a

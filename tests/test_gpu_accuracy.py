@@ -67,7 +67,9 @@ LAW_CASES = [
     ("prefill_small_tile_block_k128", 64, 256, 128, 1, True),
     ("prefill_small_tile_k128_wide", 4096, 4096, 128, 1, False),
     ("prefill_line", 4096, 4096, 256, 1, False),
+    ("prefill_line_192_wide", 4096, 6144, 256, 1, False),
     ("prefill_line_block", 4096, 4096, 512, 1, True),
+    ("prefill_line_block_column_split", 8192, 3072, 512, 1, True),
 ]
 
 
