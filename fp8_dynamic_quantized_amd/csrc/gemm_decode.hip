@@ -557,16 +557,22 @@ DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, size_t ws_cap) {
   // slower at 8 (the register kernel's token-row loads grow with the rows)
   p.line = M > 8 ? 1 : 0;
   if (p.line) {
-    // Whole-line kernel: 128 weight rows per workgroup, two workgroups per
-    // CU. Split K until there are >= 1.5 workgroups per CU, keeping at least
-    // 8 K steps per slice; long rows with fewer row blocks than CUs split to
-    // two workgroups per CU, where the slices' partial tiles are small next
-    // to the weights. (Measured on the 70B linears at 32 and 64 tokens: more
-    // slices than this lose more to the partial tiles and the last slice's
-    // reduction than they gain in balance.)
+    // Whole-line kernel: 128 weight rows per workgroup (wg0 row blocks). K
+    // is split so that the slices fill the CUs once: floor(CUs / wg0)
+    // slices; up to 32 tokens on rows shorter than 16384, at most 3 where 3
+    // already reach half the CUs; long rows (K >= 16384) with more than 32
+    // tokens take two workgroups per CU. Measured on the 70B linears at
+    // 12-64 tokens, forcing 1-12 slices: this picks the fastest count or one
+    // within 2 % for qkv, o and down. A grid a little over one workgroup per
+    // CU (qkv in 4 slices: 320) was the slowest after an unsplit K; o in 4
+    // slices (16 K steps each) was 13 % slower than in 3 up to 32 tokens and
+    // 6-12 % faster above; the 16 x 4096 -> 1024 linear (8 row blocks) was
+    // 3 % slower in 3 slices than in 4.
     const int64_t wg0 = (N + DL_BN - 1) / DL_BN;
-    const int64_t target = (K >= 16384 && wg0 < ncu) ? 2 * ncu : (3 * ncu) / 2;
-    int64_t sp = (target + wg0 - 1) / wg0;
+    int64_t sp = ncu / wg0;
+    if (K >= 16384 && M > 32) sp = (2 * ncu) / wg0;
+    if (K < 16384 && M <= 32 && sp > 3 && 3 * wg0 >= ncu / 2) sp = 3;
+    if (sp < 1) sp = 1;
     if (sp > KT / 8) sp = KT / 8;
     if (sp < 1) sp = 1;
     const size_t tile_b = (size_t)DL_BN * 16 * p.mb * 4;
