@@ -8,12 +8,12 @@
 // comes from moving half the bytes).
 //
 // Two kernels, by token count:
-//  * up to 8 rows, gemm_decode_kernel: a workgroup owns 16 weight rows and
+//  * up to 4 rows, gemm_decode_kernel: a workgroup owns 16 weight rows and
 //    one K slice; its 4 waves take interleaved 128-byte K steps with a 4-deep
 //    register prefetch of weight and token-row fragments (plain 16-byte
 //    loads, bounded only by registers), and add their partial sums in a
 //    fixed order through LDS;
-//  * 9-64 rows, gemm_decode_line_kernel: 128 weight rows per workgroup (32
+//  * 5-64 rows, gemm_decode_line_kernel: 128 weight rows per workgroup (32
 //    per wave); weights and the token rows' codes move L2 -> LDS with
 //    whole-line loads into a 3-slot ring, the token rows loaded once per
 //    workgroup and shared by its waves. Every token row then costs 1/128 of
@@ -132,7 +132,7 @@ __device__ __forceinline__ void store_out(uint16_t* __restrict__ y, const float*
 }
 
 // ---------------------------------------------------------------------------
-// Register-loading kernel (up to 8 token rows).
+// Register-loading kernel (up to 4 token rows).
 // ---------------------------------------------------------------------------
 template <bool BLOCK>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(
 
   // MFMA operand A: 16 weight rows; B: 16 token rows. Lanes of padding token
   // rows (lr >= M) get an offset past the buffer and load nothing; their
-  // outputs are dropped. M * K < 2^31 on this path (M <= 8, K <= 2^17).
+  // outputs are dropped. M * K < 2^31 on this path (M <= 4, K <= 2^17).
   const __amdgpu_buffer_rsrc_t xrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)qx, (short)0, M * K, 0x00020000);
   const uint8_t* wp = qw + (int64_t)min(n0 + lr, N - 1) * K + kg * 32;
@@ -552,10 +552,11 @@ DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, size_t ws_cap) {
 
   const int64_t KT = K / BK;
   const int64_t ncu = decode_cu_count();
-  // above 8 token rows, the whole-line kernel: on the 70B linears it was
-  // 11-20 % faster than the register kernel at 16 rows (o 8 % slower) and
-  // slower at 8 (the register kernel's token-row loads grow with the rows)
-  p.line = M > 8 ? 1 : 0;
+  // above 4 token rows, the whole-line kernel: on the 70B linears at 5-8
+  // rows it was 1-11 % faster than the register kernel on qkv, gate_up and
+  // down and 2-4 % slower on o; at 3 rows mixed (o 8 % slower); at 16 rows
+  // 11-20 % faster (the register kernel's token-row loads grow with the rows)
+  p.line = M > 4 ? 1 : 0;
   if (p.line) {
     // Whole-line kernel: 128 weight rows per workgroup (wg0 row blocks). K
     // is split so that the slices fill the CUs once: floor(CUs / wg0)

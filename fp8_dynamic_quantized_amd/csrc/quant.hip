@@ -43,8 +43,12 @@ using namespace codec;
 // Per-row quantization: one scale per row of [rows, K].
 // A team of TEAM_WAVES waves owns a row; each lane holds CH chunks of the row
 // in registers. Block = 256 threads (4 / TEAM_WAVES rows per block).
+// SPLIT (few long rows): CH blocks per row (blockIdx.y), each loading the
+// whole row for its amax but encoding and storing only its lanes' chunk y,
+// so the encoding of one row runs on CH CUs (the extra reads of the row hit
+// L2; the amax, a maximum, is the same in every block).
 // ---------------------------------------------------------------------------
-template <int CH, int TEAM_WAVES>
+template <int CH, int TEAM_WAVES, bool SPLIT = false>
 __global__ __launch_bounds__(TEAM_WAVES >= 4 ? 64 * TEAM_WAVES : 256) void quant_rows_kernel(
     const uint4* __restrict__ x, int64_t rows, int64_t K, uint2* __restrict__ q,
     float* __restrict__ scale) {
@@ -82,19 +86,19 @@ __global__ __launch_bounds__(TEAM_WAVES >= 4 ? 64 * TEAM_WAVES : 256) void quant
   float s, r, p;
   bool tiny;
   unit_scale(m, s, r, p, tiny);
-  if (tl == 0) scale[row] = s;
+  if (tl == 0 && (!SPLIT || blockIdx.y == 0)) scale[row] = s;
   uint2* qr = q + row * nch;
   if (!tiny) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int64_t c = (int64_t)i * TEAM + tl;
-      if (c < nch) qr[c] = quant8<false>(v[i], s, r, p);
+      if (c < nch && (!SPLIT || i == (int)blockIdx.y)) qr[c] = quant8<false>(v[i], s, r, p);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int64_t c = (int64_t)i * TEAM + tl;
-      if (c < nch) qr[c] = quant8<true>(v[i], s, r, p);
+      if (c < nch && (!SPLIT || i == (int)blockIdx.y)) qr[c] = quant8<true>(v[i], s, r, p);
     }
   }
 }
@@ -201,13 +205,13 @@ __global__ __launch_bounds__(256) void quant_wblock_kernel(
   }
 }
 
-template <int CH, int TW>
+template <int CH, int TW, bool SPLIT = false>
 void launch_rows(const void* x, int64_t rows, int64_t K, uint8_t* q,
                  float* scale, hipStream_t st) {
   constexpr int RPB = TW >= 4 ? 1 : 4 / TW;
   constexpr int THREADS = TW >= 4 ? 64 * TW : 256;
   const int64_t blocks = (rows + RPB - 1) / RPB;
-  hipLaunchKernelGGL((quant_rows_kernel<CH, TW>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((quant_rows_kernel<CH, TW, SPLIT>), dim3((unsigned)blocks, SPLIT ? CH : 1),
                      dim3(THREADS), 0, st, (const uint4*)x, rows, K, (uint2*)q,
                      scale);
 }
@@ -218,12 +222,14 @@ void launch_rows(const void* x, int64_t rows, int64_t K, uint8_t* q,
 void launch_quant_rows(const void* x, int64_t rows, int64_t K, uint8_t* q,
                        float* scale, hipStream_t st) {
   const int64_t nch = K / 8;
-  // Few rows (decode): a 1024-thread block per row, each thread 1-4 chunks,
-  // so the load -> amax -> quantize chain of one row is short.
+  // Few rows (decode): 1024-thread blocks, each thread 1-4 chunks, so the
+  // load -> amax -> quantize chain of one row is short; with 2 or 4 chunks,
+  // as many blocks per row, each encoding one chunk per lane (the encoding
+  // dominates: on one CU, a 28672-wide row took 5.2 us, 64 of them 8.8 us).
   if (rows <= 128 && nch > 64 && nch <= 1024 * 4) {
     if (nch <= 1024) launch_rows<1, 16>(x, rows, K, q, scale, st);
-    else if (nch <= 2048) launch_rows<2, 16>(x, rows, K, q, scale, st);
-    else launch_rows<4, 16>(x, rows, K, q, scale, st);
+    else if (nch <= 2048) launch_rows<2, 16, true>(x, rows, K, q, scale, st);
+    else launch_rows<4, 16, true>(x, rows, K, q, scale, st);
     return;
   }
   // One wave per row for short rows, else a team of 4 (or 8) waves. At

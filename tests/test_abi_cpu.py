@@ -99,14 +99,16 @@ def test_workspace_rules(L):
     for M, N, K in [(16, 1024, 16384), (1, 96, 131072), (64, 8192, 28672), (20, 100, 65536)]:
         need = F.fp8_workspace_bytes(M, N, K)
         assert need >= 16384 + 2 * 1024 and (need - 16384) % 1024 == 0, (M, N, K)
-    # 16-row weight blocks (up to 8 tokens): no split with as many blocks as
+    # 16-row weight blocks (up to 4 tokens): no split with as many blocks as
     # CUs, nor on rows shorter than 16384
     assert F.fp8_workspace_bytes(1, 57344, 8192) == 0
-    assert F.fp8_workspace_bytes(8, 10240, 8192) == 0
-    assert F.fp8_workspace_bytes(8, 1024, 4096) == 0
-    # 128-row weight blocks (9-64 tokens): few blocks split K
+    assert F.fp8_workspace_bytes(4, 10240, 8192) == 0
+    assert F.fp8_workspace_bytes(4, 1024, 4096) == 0
+    # 128-row weight blocks (5-64 tokens): fewer blocks than CUs split K
+    assert F.fp8_workspace_bytes(8, 10240, 8192) > 0
     assert F.fp8_workspace_bytes(16, 1024, 4096) > 0
     assert F.fp8_workspace_bytes(32, 1024, 4096) > 0
+    assert F.fp8_workspace_bytes(8, 57344, 8192) == 0      # 448 blocks: no split
     assert F.fp8_workspace_bytes(4096, 4096, 4096) == 0
     assert F.fp8_workspace_bytes(16, 1024, 16384, flags=F.FORCE_PREFILL) == 0
     assert F.fp8_workspace_bytes(16, 1024, 100) == 0       # invalid K -> 0

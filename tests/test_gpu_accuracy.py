@@ -58,8 +58,9 @@ def tile(a: np.ndarray, rows: int) -> np.ndarray:
 
 # (name, M, N, K, flags, block): which kernel runs follows from the shape
 LAW_CASES = [
-    ("decode_register", 8, 256, 512, 2, False),
-    ("decode_register_block", 8, 256, 512, 2, True),
+    ("decode_register", 4, 256, 512, 2, False),
+    ("decode_register_block", 4, 256, 512, 2, True),
+    ("decode_line_8_rows", 8, 4096, 512, 2, False),
     ("decode_line_16_rows", 16, 4096, 512, 2, False),
     ("decode_line", 48, 256, 512, 2, False),
     ("decode_block", 48, 256, 512, 2, True),
@@ -76,7 +77,7 @@ LAW_CASES = [
 @pytest.mark.parametrize("name,M,N,K,flags,block", LAW_CASES, ids=[c[0] for c in LAW_CASES])
 def test_accumulation_law_constructed(F, name, M, N, K, flags, block):
     say(f"law {name} {M}x{N}x{K}")
-    R = C = 8
+    R, C = min(8, M), 8
     vx, vw = constructed(R, C, K, seed=K + M)
     exact = vx @ vw.T
     decode = flags == 2

@@ -371,8 +371,9 @@ def block_ref_rows(qx, sx, qw, sw, rows, cols):
 
 
 @pytest.mark.parametrize("M,N,flags", [(8192, 8192, 1), (512, 512, 1), (64, 512, 1), (48, 512, 2),
-                                       (8, 512, 2)],
-                         ids=["wide_tiles", "narrow_tiles", "narrow_m64", "decode", "decode_8_rows"])
+                                       (8, 512, 2), (4, 512, 2)],
+                         ids=["wide_tiles", "narrow_tiles", "narrow_m64", "decode", "decode_8_rows",
+                              "decode_4_rows"])
 def test_block_factor_extremes(F, M, N, flags):
     """Block factors sx * sw spanning the fp32 range, made by multiplying a
     row's own group scales (so y stays of order 1, as in real data): later
@@ -488,8 +489,8 @@ DECODE_CASES = [(1, 8192, 8192), (5, 100, 1664), (16, 1024, 4096), (17, 520, 320
                 (1, 8192, 28672),
                 # register kernel split on a long row at one token
                 (1, 64, 16384),
-                # whole-line kernel with one 16-row token block (9-16
-                # tokens), in 2 and 16 K slices
+                # whole-line kernel with one 16-row token block (5-16
+                # tokens), in 2 and 8 K slices
                 (9, 4500, 2560), (12, 4096, 16384),
                 # whole-line kernel on long rows (8, 16 and 20 K slices; more
                 # than 16 slices take the reduction's general loop)
