@@ -30,16 +30,18 @@
 // magnitude >= 16 and the rest, and the two halves go through two MFMAs into
 // the same accumulator: a group's small products are then cut relative to
 // small ones only. The split is exact (the halves have disjoint support) and
-// costs one more MFMA per step, which the weight stream hides.
+// costs one more MFMA and a few bit operations per step, which the weight
+// stream mostly hides.
 //
 // Split K. When the row blocks alone leave the CUs short of work, K is
 // split across the grid (grid.y). Each slice writes its fp32 partial tile to
 // the workspace and counts itself on the tile's counter; the last slice to
 // arrive adds all partials in slice order (so the result does not depend on
 // the arrival order) and applies the epilogue, then clears the counter. The
-// partials are written and read with agent-scope atomic stores and loads,
-// which go to the memory side of the per-XCD L2s, and every store has
-// completed before its slice is counted.
+// partials are written and read with the sc1 cache policy (as agent-scope
+// atomic accesses are), so they reach the memory side of the per-XCD L2s,
+// and every store has completed before its slice is counted (a relaxed
+// agent-scope atomic add on the counter).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
