@@ -13,8 +13,12 @@
 //    register prefetch of weight and token-row fragments (plain 16-byte
 //    loads, bounded only by registers), and add their partial sums in a
 //    fixed order through LDS;
-//  * 5-64 rows, gemm_decode_line_kernel: 128 weight rows per workgroup (32
-//    per wave); weights and the token rows' codes move L2 -> LDS with
+//  * 5-64 rows, gemm_decode_line_kernel: 128 weight rows per workgroup
+//    (32 per wave against every token row; at 49-64 rows each wave instead
+//    takes its own 16 token rows against all 128 weight rows, which splits
+//    a token fragment once per step instead of four times and cut the 70B
+//    qkv linear at 64 tokens from 29.7 to 25.2 us); weights and the token
+//    rows' codes move L2 -> LDS with
 //    whole-line loads into a 3-slot ring, the token rows loaded once per
 //    workgroup and shared by its waves. Every token row then costs 1/128 of
 //    the weight bytes, against 1/16 in the register kernel, whose token-row
@@ -303,7 +307,7 @@ constexpr int DL_NSL = 3;                // ring slots
 
 __device__ __forceinline__ int dswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-template <int MB, bool BLOCK>
+template <int MB, bool BLOCK, bool TW>
 __global__ __launch_bounds__(256, 2) void gemm_decode_line_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint8_t* __restrict__ qw, const float* __restrict__ sw,
@@ -316,11 +320,20 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_line_kernel(
   constexpr int XI = (2 * MB + 3) / 4;               // token-row loads per wave (>= 1)
   constexpr int WI = DL_BN / 32;                     // weight loads per wave
   constexpr int L = XI + WI + (BLOCK ? 1 : 0);
+  // The WG's MFMA blocks: 8 weight fragments x MB token fragments (16 rows
+  // each). A wave takes NWF weight fragments from W0 and NTF token fragments
+  // from T0: two weight fragments against every token fragment, or (TW, 64
+  // token rows) every weight fragment against its own token fragment, so
+  // that each wave splits one token fragment a step instead of all four.
+  static_assert(!TW || MB == 4, "token-row waves need 4 token fragments");
+  constexpr int NWF = TW ? 8 : 2;
+  constexpr int NTF = TW ? 1 : MB;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   __shared__ unsigned last_flag;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n0 = blockIdx.x * DL_BN;
+  const int W0 = TW ? 0 : 2 * wave, T0 = TW ? wave : 0;
   const int split = blockIdx.y, splits = gridDim.y;
   const int KP = K / BK;
   const int p0 = split * kp_per_split;
@@ -391,11 +404,11 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_line_kernel(
     return r;
   };
 
-  v4f acc[2][MB];
+  v4f acc[NWF][NTF];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NWF; ++i)
 #pragma unroll
-    for (int j = 0; j < MB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NTF; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
   for (int q = 0; q < DL_NSL - 1; ++q) issue(q);
@@ -405,19 +418,19 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_line_kernel(
     asm volatile("s_barrier" ::: "memory");
     issue(p + DL_NSL - 1);
     const uint8_t* sb = smem + (p % DL_NSL) * SLOT;
-    v8i a[2], bl[MB], bh[MB];
+    v8i a[NWF], bl[NTF], bh[NTF];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = rd(sb + XB + (32 * wave + 16 * i) * BK);
+    for (int i = 0; i < NWF; ++i) a[i] = rd(sb + XB + 16 * (W0 + i) * BK);
 #pragma unroll
-    for (int j = 0; j < MB; ++j) split_big(rd(sb + 16 * j * BK), bl[j], bh[j]);
+    for (int j = 0; j < NTF; ++j) split_big(rd(sb + 16 * (T0 + j) * BK), bl[j], bh[j]);
     if constexpr (BLOCK) {   // the group's scales from the slot
       const float* scl = reinterpret_cast<const float*>(sb + SB);
       const float swg = scl[64];
 #pragma unroll
-      for (int j = 0; j < MB; ++j) {
-        const float f = scl[16 * j + fr] * swg;
+      for (int j = 0; j < NTF; ++j) {
+        const float f = scl[16 * (T0 + j) + fr] * swg;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NWF; ++i) {
           v4f pr = mfma_e4m3_16x16x128(a[i], bl[j], v4f{0.f, 0.f, 0.f, 0.f});
           pr = mfma_e4m3_16x16x128(a[i], bh[j], pr);
 #pragma unroll
@@ -426,9 +439,9 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_line_kernel(
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NWF; ++i)
 #pragma unroll
-        for (int j = 0; j < MB; ++j) {
+        for (int j = 0; j < NTF; ++j) {
           acc[i][j] = mfma_e4m3_16x16x128(a[i], bl[j], acc[i][j]);
           acc[i][j] = mfma_e4m3_16x16x128(a[i], bh[j], acc[i][j]);
         }
@@ -439,12 +452,12 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_line_kernel(
   // D[n, m]: lane l holds n = 16 i + 4 (l / 16) + r of the wave's rows, m = 16 j + l % 16
   if (splits == 1) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int n = n0 + 32 * wave + 16 * i + 4 * kq;
+    for (int i = 0; i < NWF; ++i) {
+      const int n = n0 + 16 * (W0 + i) + 4 * kq;
       if (n >= N) continue;
 #pragma unroll
-      for (int j = 0; j < MB; ++j) {
-        const int m = 16 * j + fr;
+      for (int j = 0; j < NTF; ++j) {
+        const int m = 16 * (T0 + j) + fr;
         if (m >= M) continue;
         const float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
         store_out<BLOCK>(y, sx, sw, m, n, N, v);
@@ -455,15 +468,15 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_line_kernel(
   // split K: publish this slice's partial tile (lane order: [wave][i][j]
   // [lane] x 16 bytes), count it; the last slice adds all slices' tiles in
   // slice order
-  constexpr uint32_t TILE_B = 4u * 2u * MB * 1024u;   // bytes of one slice's tile
+  constexpr uint32_t TILE_B = 4u * NWF * NTF * 1024u;   // bytes of one slice's tile
   float* tile = part + (int64_t)blockIdx.x * splits * (TILE_B / 4);
   const __amdgpu_buffer_rsrc_t pr = part_rsrc(tile, (uint32_t)splits * TILE_B);
-  const uint32_t lo_off = (uint32_t)wave * 2u * MB * 1024u + (uint32_t)lane * 16u;
+  const uint32_t lo_off = (uint32_t)wave * NWF * NTF * 1024u + (uint32_t)lane * 16u;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NWF; ++i)
 #pragma unroll
-    for (int j = 0; j < MB; ++j)
-      st_part(pr, (uint32_t)split * TILE_B + lo_off + (uint32_t)(i * MB + j) * 1024u, acc[i][j]);
+    for (int j = 0; j < NTF; ++j)
+      st_part(pr, (uint32_t)split * TILE_B + lo_off + (uint32_t)(i * NTF + j) * 1024u, acc[i][j]);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's stores have completed
   __syncthreads();                            // ... and every other wave's
   if (tid == 0)
@@ -474,31 +487,31 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_line_kernel(
   // slice by slice, all of a slice's fragments in flight together (and the
   // next slice's issued before this one's adds): about one memory latency
   // per slice
-  v4f nxt[2][MB];
+  v4f nxt[NWF][NTF];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NWF; ++i)
 #pragma unroll
-    for (int j = 0; j < MB; ++j) acc[i][j] = ld_part(pr, lo_off + (uint32_t)(i * MB + j) * 1024u);
+    for (int j = 0; j < NTF; ++j) acc[i][j] = ld_part(pr, lo_off + (uint32_t)(i * NTF + j) * 1024u);
   for (int k = 1; k < splits; ++k) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NWF; ++i)
 #pragma unroll
-      for (int j = 0; j < MB; ++j)
-        nxt[i][j] = ld_part(pr, (uint32_t)k * TILE_B + lo_off + (uint32_t)(i * MB + j) * 1024u);
+      for (int j = 0; j < NTF; ++j)
+        nxt[i][j] = ld_part(pr, (uint32_t)k * TILE_B + lo_off + (uint32_t)(i * NTF + j) * 1024u);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NWF; ++i)
 #pragma unroll
-      for (int j = 0; j < MB; ++j)
+      for (int j = 0; j < NTF; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[i][j][r] += nxt[i][j][r];
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int n = n0 + 32 * wave + 16 * i + 4 * kq;
+  for (int i = 0; i < NWF; ++i) {
+    const int n = n0 + 16 * (W0 + i) + 4 * kq;
     if (n >= N) continue;
 #pragma unroll
-    for (int j = 0; j < MB; ++j) {
-      const int m = 16 * j + fr;
+    for (int j = 0; j < NTF; ++j) {
+      const int m = 16 * (T0 + j) + fr;
       if (m >= M) continue;
       const float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
       store_out<BLOCK>(y, sx, sw, m, n, N, v);
@@ -508,7 +521,7 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_line_kernel(
     __hip_atomic_store(cnt + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MB, bool BLOCK>
+template <int MB, bool BLOCK, bool TW = false>
 void launch_line_dec(const uint8_t* qx, const float* sx, const uint8_t* qw,
                      const float* sw, void* y, float* part, unsigned* cnt, int64_t M,
                      int64_t N, int64_t K, const DecodePlan& p, hipStream_t st) {
@@ -516,11 +529,11 @@ void launch_line_dec(const uint8_t* qx, const float* sx, const uint8_t* qw,
   static std::once_flag once;
   std::call_once(once, [] {
     (void)hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_decode_line_kernel<MB, BLOCK>),
+        reinterpret_cast<const void*>(&gemm_decode_line_kernel<MB, BLOCK, TW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   });
   const unsigned gx = (unsigned)((N + DL_BN - 1) / DL_BN);
-  hipLaunchKernelGGL((gemm_decode_line_kernel<MB, BLOCK>), dim3(gx, (unsigned)p.splits),
+  hipLaunchKernelGGL((gemm_decode_line_kernel<MB, BLOCK, TW>), dim3(gx, (unsigned)p.splits),
                      dim3(256), smem, st, qx, sx, qw, sw, (uint16_t*)y, part, cnt, (int)M,
                      (int)N, (int)K, p.kt_per_split);
 }
@@ -633,8 +646,8 @@ void launch_gemm_decode(const uint8_t* qx, const float* sx, const uint8_t* qw,
                   : launch_line_dec<2, false>(qx, sx, qw, sw, y, part, cnt, M, N, K, p, st); break;
     case 3: block ? launch_line_dec<3, true>(qx, sx, qw, sw, y, part, cnt, M, N, K, p, st)
                   : launch_line_dec<3, false>(qx, sx, qw, sw, y, part, cnt, M, N, K, p, st); break;
-    default: block ? launch_line_dec<4, true>(qx, sx, qw, sw, y, part, cnt, M, N, K, p, st)
-                   : launch_line_dec<4, false>(qx, sx, qw, sw, y, part, cnt, M, N, K, p, st); break;
+    default: block ? launch_line_dec<4, true, true>(qx, sx, qw, sw, y, part, cnt, M, N, K, p, st)
+                   : launch_line_dec<4, false, true>(qx, sx, qw, sw, y, part, cnt, M, N, K, p, st); break;
   }
 }
 

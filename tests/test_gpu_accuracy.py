@@ -64,6 +64,8 @@ LAW_CASES = [
     ("decode_line_16_rows", 16, 4096, 512, 2, False),
     ("decode_line", 48, 256, 512, 2, False),
     ("decode_block", 48, 256, 512, 2, True),
+    ("decode_line_64_rows", 64, 256, 512, 2, False),
+    ("decode_block_64_rows", 64, 256, 512, 2, True),
     ("prefill_small_tile", 64, 256, 512, 1, False),
     ("prefill_small_tile_block_k128", 64, 256, 128, 1, True),
     ("prefill_small_tile_k128_wide", 4096, 4096, 128, 1, False),
