@@ -69,7 +69,13 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 //    its factor is formed a few MFMAs later, so the matrix core does not
 //    wait for those reads.
 //  * Epilogue from registers: scale, round to bf16, and pair lanes l and l+32
-//    with v_permlane32_swap so each lane stores 16 contiguous bytes.
+//    with v_permlane32_swap so each lane holds 16 contiguous bytes. In a tile
+//    with no ragged edge, v_permlane16_swap and a DPP row rotation then
+//    regroup two 32-column fragments so that each store instruction writes
+//    8 rows x 128 bytes (whole lines) with the non-temporal hint: Y (a round
+//    of tiles writes about one L2 of it per XCD) then streams past the L2
+//    instead of evicting X and W. Whole lines without the hint, or the hint
+//    on 32-byte row pieces, gained nothing or lost.
 //  * A workgroup may walk several tiles (blockIdx.x, + gridDim.x, ...): after
 //    a tile's last step and one barrier, the next tile's scales (other
 //    buffer) and first NSL pairs are issued, so they load during this tile's
@@ -490,44 +496,103 @@ __global__ __launch_bounds__((64 * LineCfg<BLOCK, BNP>::NW), 1) void gemm_prefil
     float smv[DMJ];
 #pragma unroll
     for (int j = 0; j < DMJ; ++j) smv[j] = BLOCK ? fcur[j] : scl[wm * DTM + 32 * j + elr];
-    // j outer, then i and qp: a lane's eight stores of one row (the wave's
-    // 2 * DTN bytes of it) go out back to back, so each 128-byte line of Y is
-    // completed by consecutive stores rather than written back in pieces
+    // A tile inside Y (no ragged edge, 16-byte aligned rows) stores whole
+    // 128-byte lines with the non-temporal hint; other tiles store 16-byte
+    // pieces, masked per element at the edges.
+    const bool full = em0 + BM <= M && en0 + BN <= N && vec;   // uniform
+    // (i, qp) -> 16 bytes of this lane's row: bf16 of the scaled
+    // accumulators, lanes l and l+32 exchanging halves with
+    // v_permlane32_swap so lane l holds n = 32 i + 16 qp + 8 (l / 32) + 0..7
+    // of row m = 32 j + l % 32
+    auto pack16 = [&](int i, int j, int qp, float sm, const float4 (&s4)[4], uint32_t (&o)[4]) {
+      uint32_t w[2][2];   // [q of the pair][dword]
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int q = 2 * qp + u;
+        w[u][0] = pk_bf16_rne(acc[i][j][4 * q + 0] * sm * s4[q].x, acc[i][j][4 * q + 1] * sm * s4[q].y);
+        w[u][1] = pk_bf16_rne(acc[i][j][4 * q + 2] * sm * s4[q].z, acc[i][j][4 * q + 3] * sm * s4[q].w);
+      }
+      // lane l (kh 0) keeps its q = 2qp values and takes lane l+32's; lane
+      // l+32 keeps its q = 2qp+1 values and takes lane l's
+      const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
+      o[0] = s0[0]; o[1] = s1[0]; o[2] = s0[1]; o[3] = s1[1];
+    };
+    auto col_scales = [&](int i, float4 (&s4)[4]) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        s4[q] = BLOCK ? make_float4(1.f, 1.f, 1.f, 1.f)
+                      : *reinterpret_cast<const float4*>(scl + 256 + wn * DTN + 32 * i + 8 * q + 4 * ekh);
+    };
+    // j outer, then i and qp: a lane's stores of one row (the wave's
+    // 2 * DTN bytes of it) go out back to back
 #pragma unroll
     for (int j = 0; j < DMJ; ++j) {
       const int m = em0 + wm * DTM + 32 * j + elr;
       const float sm = smv[j];
 #pragma unroll
       for (int i = 0; i < DNI; ++i) {
-        float4 s4[4];
+        if (full && (i & 1) == 0 && i + 1 < DNI) {
+          // Fragments i and i+1 (64 columns) of rows 32 j .. 32 j + 31 as 4
+          // stores of 8 rows x 128 bytes. After pack16, lane bits 0-4 are
+          // row bits 0-4 and lane bit 5 is column bit 3; qp is column bit 4
+          // and i & 1 column bit 5. v_permlane16_swap exchanges lane bit 4
+          // with qp, a row_ror:8 DPP move lane bit 3 with i & 1: the slot
+          // [a][b] then holds rows 16 b + 8 a + (l & 7) and lane l columns
+          // 32 (l>>3 & 1) + 16 (l>>4 & 1) + 8 (l>>5) + 0..7.
+          uint32_t r[2][2][4];   // [i & 1 -> row bit 3][qp -> row bit 4][dword]
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          s4[q] = BLOCK ? make_float4(1.f, 1.f, 1.f, 1.f)
-                        : *reinterpret_cast<const float4*>(scl + 256 + wn * DTN + 32 * i + 8 * q + 4 * ekh);
+          for (int a = 0; a < 2; ++a) {
+            float4 s4[4];
+            col_scales(i + a, s4);
 #pragma unroll
-        for (int qp = 0; qp < 2; ++qp) {
-          uint32_t w[2][2];   // [q of the pair][dword]
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int q = 2 * qp + u;
-            w[u][0] = pk_bf16_rne(acc[i][j][4 * q + 0] * sm * s4[q].x, acc[i][j][4 * q + 1] * sm * s4[q].y);
-            w[u][1] = pk_bf16_rne(acc[i][j][4 * q + 2] * sm * s4[q].z, acc[i][j][4 * q + 3] * sm * s4[q].w);
+            for (int qp = 0; qp < 2; ++qp) pack16(i + a, j, qp, sm, s4, r[a][qp]);
           }
-          // lane l (kh 0) keeps its q = 2qp values and takes lane l+32's; lane
-          // l+32 keeps its q = 2qp+1 values and takes lane l's
-          const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
-          const auto s1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
-          const uint4 o = make_uint4(s0[0], s1[0], s0[1], s1[1]);
-          const int n = en0 + wn * DTN + 32 * i + 16 * qp + 8 * ekh;
-          if (m < M) {
-            uint16_t* out = y + (int64_t)m * ldy + n;
-            if (vec && n + 7 < N) {
-              *reinterpret_cast<uint4*>(out) = o;
-            } else {
-              const uint32_t w4[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
-              for (int e = 0; e < 8; ++e)
-                if (n + e < N) out[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+          for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              const auto t = __builtin_amdgcn_permlane16_swap(r[a][0][d], r[a][1][d], false, false);
+              r[a][0][d] = t[0];
+              r[a][1][d] = t[1];
+            }
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              const uint32_t x = r[0][b][d], z = r[1][b][d];
+              // lanes with bit 3 set take z from lane ^ 8, the others x
+              r[0][b][d] = (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)z, 0x128, 0xF, 0xC, false);
+              r[1][b][d] = (uint32_t)__builtin_amdgcn_update_dpp((int)z, (int)x, 0x128, 0xF, 0x3, false);
+            }
+          const int cn = en0 + wn * DTN + 32 * i + 32 * ((eln >> 3) & 1) + 16 * ((eln >> 4) & 1) +
+                         8 * (eln >> 5);
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+              const int rm = em0 + wm * DTM + 32 * j + 16 * b + 8 * a + (eln & 7);
+              const u32x4 v = {r[a][b][0], r[a][b][1], r[a][b][2], r[a][b][3]};
+              __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(y + (int64_t)rm * ldy + cn));
+            }
+        } else if (!full || (DNI & 1)) {
+          if (full && i + 1 != DNI) continue;   // (stored with fragment i - 1)
+          float4 s4[4];
+          col_scales(i, s4);
+#pragma unroll
+          for (int qp = 0; qp < 2; ++qp) {
+            uint32_t o[4];
+            pack16(i, j, qp, sm, s4, o);
+            const int n = en0 + wn * DTN + 32 * i + 16 * qp + 8 * ekh;
+            if (m < M) {
+              uint16_t* out = y + (int64_t)m * ldy + n;
+              if (vec && n + 7 < N) {
+                *reinterpret_cast<uint4*>(out) = make_uint4(o[0], o[1], o[2], o[3]);
+              } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                  if (n + e < N) out[e] = (uint16_t)(o[e >> 1] >> (16 * (e & 1)));
+              }
             }
           }
         }
