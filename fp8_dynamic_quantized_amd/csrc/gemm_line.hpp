@@ -496,10 +496,14 @@ __global__ __launch_bounds__((64 * LineCfg<BLOCK, BNP>::NW), 1) void gemm_prefil
     float smv[DMJ];
 #pragma unroll
     for (int j = 0; j < DMJ; ++j) smv[j] = BLOCK ? fcur[j] : scl[wm * DTM + 32 * j + elr];
-    // A tile inside Y (no ragged edge, 16-byte aligned rows) stores whole
-    // 128-byte lines with the non-temporal hint; other tiles store 16-byte
-    // pieces, masked per element at the edges.
-    const bool full = em0 + BM <= M && en0 + BN <= N && vec;   // uniform
+    // A tile inside Y (no ragged edge, rows starting on 128-byte lines)
+    // stores whole lines with the non-temporal hint, two 32-column fragments
+    // (64 columns, one line of a row) at a time; other tiles, and a fragment
+    // left without a line-aligned partner (256 x 192 tiles: the wave's third),
+    // store 16-byte pieces, masked per element at the edges.
+    const bool full = em0 + BM <= M && en0 + BN <= N && (ldy & 63) == 0 &&
+                      ((uintptr_t)y & 127) == 0;   // uniform
+    const int fo = (wn * DNI) & 1;   // fragment i starts a line when (i + fo) is even
     // (i, qp) -> 16 bytes of this lane's row: bf16 of the scaled
     // accumulators, lanes l and l+32 exchanging halves with
     // v_permlane32_swap so lane l holds n = 32 i + 16 qp + 8 (l / 32) + 0..7
@@ -532,7 +536,8 @@ __global__ __launch_bounds__((64 * LineCfg<BLOCK, BNP>::NW), 1) void gemm_prefil
       const float sm = smv[j];
 #pragma unroll
       for (int i = 0; i < DNI; ++i) {
-        if (full && (i & 1) == 0 && i + 1 < DNI) {
+        const bool lead = ((i + fo) & 1) == 0;
+        if (full && lead && i + 1 < DNI) {
           // Fragments i and i+1 (64 columns) of rows 32 j .. 32 j + 31 as 4
           // stores of 8 rows x 128 bytes. After pack16, lane bits 0-4 are
           // row bits 0-4 and lane bit 5 is column bit 3; qp is column bit 4
@@ -575,8 +580,7 @@ __global__ __launch_bounds__((64 * LineCfg<BLOCK, BNP>::NW), 1) void gemm_prefil
               const u32x4 v = {r[a][b][0], r[a][b][1], r[a][b][2], r[a][b][3]};
               __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(y + (int64_t)rm * ldy + cn));
             }
-        } else if (!full || (DNI & 1)) {
-          if (full && i + 1 != DNI) continue;   // (stored with fragment i - 1)
+        } else if (!full || (lead && i + 1 == DNI) || (!lead && i == 0)) {
           float4 s4[4];
           col_scales(i, s4);
 #pragma unroll
