@@ -195,7 +195,11 @@ WIDE_RAGGED = [
     (4173, 3853, 384), (4097, 4104, 256), (4352, 4096, 1152), (4352, 4790, 384),
     (4000, 6144, 256),
     # 256 x 256 tiles: one round; two rounds with two workgroups taking one tile
-    (4000, 3990, 384), (4352, 7630, 256)]
+    (4000, 3990, 384), (4352, 7630, 256),
+    # 256 x 256 tiles on line-aligned rows (N % 64 == 0): the full tiles store
+    # whole 128-byte lines, the last tile row (M ragged) 16-byte pieces;
+    # 510 tiles, so workgroups walk two tiles each (254 of them)
+    (4300, 7680, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", WIDE_RAGGED)
