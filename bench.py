@@ -12,9 +12,13 @@ resident in HBM.
 Prints one JSON line (value = whole-step TFLOP/s, 2*M*N*K per linear).
 Also reported:
   roofline      the dominant kernel (the gate_up GEMM), timed with HIP events
-                on the stream it runs on; HBM traffic from the committed
-                counter summary when it matches the current kernel source;
-  per_linear    per-linear quantizer and GEMM kernel times;
+                on the stream it runs on, around that launch only, in every
+                timed step; HBM traffic from the committed counter summary
+                when it matches the current kernel source;
+  per_linear    per-linear quantizer and GEMM kernel times, from events around
+                every launch in a separate pass after the timed steps (a timed
+                event in the stream waits for the launch before it, so twelve
+                of them per step would add their own stalls to the step);
   decode        the Llama-3.1-70B decode linears at M in {1, 8, 32, 64}:
                 end-to-end fp8_linear weight GB/s with cold weights
                 (rotated copies well beyond the 256 MB last-level cache);
@@ -165,38 +169,52 @@ def bench_prefill(F, torch, steps, warmup, only=None):
     flops_step = sum(2 * M * L["N"] * L["K"] for L in layers)
     stream = torch.cuda.current_stream()        # the stream every launch uses
 
-    def step(ev=None):
+    dom = [i for i, L in enumerate(layers) if L["name"] == "gate_up"][0]
+
+    def step(ev=None, every=False):
+        # ev[i] = (before the quantizer, between, after the GEMM) of linear i;
+        # recorded for the dominant linear's GEMM only, or (every) for all
         for i, L in enumerate(layers):
-            if ev is not None:
+            if ev is not None and every:
                 ev[i][0].record(stream)
             F.fp8_quant_act(L["x"], q=L["qx"], scale=L["sx"])
-            if ev is not None:
+            if ev is not None and (every or i == dom):
                 ev[i][1].record(stream)
             F.fp8_gemm(L["qx"], L["sx"], L["qw"], L["sw"], y=L["y"])
-            if ev is not None:
+            if ev is not None and (every or i == dom):
                 ev[i][2].record(stream)
+
+    def new_events(n):
+        return [[[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                 for _ in layers] for _ in range(n)]
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            for _ in layers] for _ in range(steps)]
+    evs = new_events(steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
         step(evs[k])
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    dom_ms = np.mean([evs[k][dom][1].elapsed_time(evs[k][dom][2]) for k in range(steps)])
 
+    # per-linear breakdown: a separate pass, events around every launch
+    diag = max(5, min(steps, 20))
+    evd = new_events(diag)
+    for k in range(diag):
+        step(evd[k], every=True)
+    torch.cuda.synchronize()
     quant_ms = np.zeros(len(layers))
     gemm_ms = np.zeros(len(layers))
-    for k in range(steps):
+    for k in range(diag):
         for i in range(len(layers)):
-            quant_ms[i] += evs[k][i][0].elapsed_time(evs[k][i][1])
-            gemm_ms[i] += evs[k][i][1].elapsed_time(evs[k][i][2])
-    quant_ms /= steps
-    gemm_ms /= steps
+            quant_ms[i] += evd[k][i][0].elapsed_time(evd[k][i][1])
+            gemm_ms[i] += evd[k][i][1].elapsed_time(evd[k][i][2])
+    quant_ms /= diag
+    gemm_ms /= diag
 
     per_layer = {}
     for i, L in enumerate(layers):
@@ -208,12 +226,11 @@ def bench_prefill(F, torch, steps, warmup, only=None):
             "quant_us": round(quant_ms[i] * 1e3, 2),
             "quant_gbs": round(qbytes / (quant_ms[i] * 1e-3) / 1e9, 1),
         }
-    dom = [i for i, L in enumerate(layers) if L["name"] == "gate_up"][0]
     Ld = layers[dom]
-    achieved = 2 * M * Ld["N"] * Ld["K"] / (gemm_ms[dom] * 1e-3) / 1e12
+    achieved = 2 * M * Ld["N"] * Ld["K"] / (dom_ms * 1e-3) / 1e12
     res = {"M": M, "shapes": [[L["name"], L["K"], L["N"]] for L in layers],
            "value": flops_step * steps / dt / 1e12, "ms_per_step": dt / steps * 1e3,
-           "achieved": achieved, "dom_us": gemm_ms[dom] * 1e3,
+           "achieved": achieved, "dom_us": dom_ms * 1e3,
            "dom_shape": (M, Ld["K"], Ld["N"]), "per_layer": per_layer}
     del layers
     torch.cuda.empty_cache()
@@ -845,6 +862,10 @@ def main():
             "avg_launch_us": round(pre["dom_us"], 2),
         },
         "per_linear": pre["per_layer"],
+        "per_linear_protocol": ("HIP events around every launch, in a pass after the timed "
+                                "steps; each event waits for the launch before it, so the GPU "
+                                "idles briefly between launches and the GEMMs there run at a "
+                                "higher clock than in the timed steps"),
     }
     if not args.no_decode:
         out["decode"] = bench_decode(F, torch)
