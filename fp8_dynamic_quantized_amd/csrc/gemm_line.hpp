@@ -566,7 +566,9 @@ __global__ __launch_bounds__((64 * LineCfg<BLOCK, BNP>::NW), 1) void gemm_prefil
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
               const uint32_t x = r[0][b][d], z = r[1][b][d];
-              // lanes with bit 3 set take z from lane ^ 8, the others x
+              // r[0]: lanes with bit 3 set take z from lane ^ 8, the others
+              // keep x; r[1]: lanes with bit 3 clear take x from lane ^ 8,
+              // the others keep z
               r[0][b][d] = (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)z, 0x128, 0xF, 0xC, false);
               r[1][b][d] = (uint32_t)__builtin_amdgcn_update_dpp((int)z, (int)x, 0x128, 0xF, 0x3, false);
             }
