@@ -375,9 +375,9 @@ def block_ref_rows(qx, sx, qw, sw, rows, cols):
 
 
 @pytest.mark.parametrize("M,N,flags", [(8192, 8192, 1), (512, 512, 1), (64, 512, 1), (48, 512, 2),
-                                       (8, 512, 2), (4, 512, 2)],
+                                       (8, 512, 2), (4, 512, 2), (64, 512, 2), (57, 512, 2)],
                          ids=["wide_tiles", "narrow_tiles", "narrow_m64", "decode", "decode_8_rows",
-                              "decode_4_rows"])
+                              "decode_4_rows", "decode_64_rows", "decode_57_rows"])
 def test_block_factor_extremes(F, M, N, flags):
     """Block factors sx * sw spanning the fp32 range, made by multiplying a
     row's own group scales (so y stays of order 1, as in real data): later
@@ -388,7 +388,9 @@ def test_block_factor_extremes(F, M, N, flags):
     product underflows to 0), factors rising by 2^10 and falling by 2^12 per
     group, and unchanged rows. Codes are those of the synthetic activations;
     y within tolerance of the oracle on sampled rows and columns (8192 x 8192
-    runs the 256 x 256 whole-line tiles, 512 x 512 the 256 x 128 ones)."""
+    runs the 256 x 256 whole-line tiles, 512 x 512 the 256 x 128 ones; 57
+    and 64 decode rows the layout where each wave owns 16 token rows, the
+    last wave's partly past M at 57)."""
     K = 1024
     G = K // 128
     say(f"block factor extremes {M}x{N} flags={flags}")
