@@ -16,9 +16,9 @@ Also reported:
                 timed step; HBM traffic from the committed counter summary
                 when it matches the current kernel source;
   per_linear    per-linear quantizer and GEMM kernel times, from events around
-                every launch in a separate pass after the timed steps (a timed
-                event in the stream waits for the launch before it, so twelve
-                of them per step would add their own stalls to the step);
+                every launch in a separate pass after the timed steps (timed
+                events in the stream leave short idle gaps between launches,
+                which twelve of them per step would add to the step);
   decode        the Llama-3.1-70B decode linears at M in {1, 8, 32, 64}:
                 end-to-end fp8_linear weight GB/s with cold weights
                 (rotated copies well beyond the 256 MB last-level cache);
@@ -863,9 +863,8 @@ def main():
         },
         "per_linear": pre["per_layer"],
         "per_linear_protocol": ("HIP events around every launch, in a pass after the timed "
-                                "steps; each event waits for the launch before it, so the GPU "
-                                "idles briefly between launches and the GEMMs there run at a "
-                                "higher clock than in the timed steps"),
+                                "steps; the events leave short idle gaps between launches, so "
+                                "the GEMMs there run at a higher clock than in the timed steps"),
     }
     if not args.no_decode:
         out["decode"] = bench_decode(F, torch)
