@@ -17,7 +17,8 @@
 // The bf16 rounding of h is exact (the correctly rounded value of the real
 // formula): h is formed in fp32 with a few ulps of error and rounded to bf16
 // directly unless it lies within 8 fp32 ulps of a bf16 rounding midpoint,
-// is tiny, or (SwiGLU) |g| > 64; those elements are formed again in fp64,
+// is tiny, or an fp32 intermediate left its normal range (SwiGLU: |g| > 64
+// or |g*u| > 2^127; RMSNorm: x * r tiny); those elements are formed again in fp64,
 // where a near-midpoint SwiGLU value is decided by the exact identity
 //   h - m = s * ((g*u - m) - m * e^-g),  s = 1 / (1 + e^-g) > 0,
 // in which g*u - m is exact in fp64. The quantization that follows is the
@@ -113,10 +114,12 @@ __device__ __forceinline__ float silu_recip(float g) {
   return __builtin_amdgcn_rcpf(1.0f + exp_neg(g));
 }
 
-// Elements the fast value cannot decide: |g| > 64, h near a bf16 rounding
-// midpoint, or h tiny while g*u is not zero.
+// Elements the fast value cannot decide: |g| > 64, g*u past 2^127 (it may
+// have overflowed fp32 while h = silu(g) * u is still a finite bf16), h near
+// a bf16 rounding midpoint, or h tiny while g*u is not zero.
 __device__ __forceinline__ bool silu_flag(float g, float gu, float h) {
-  return (__builtin_fabsf(g) > 64.0f) | near_mid16(h) | (tiny32(h) & (gu != 0.0f));
+  return (__builtin_fabsf(g) > 64.0f) | (__builtin_fabsf(gu) > 0x1p127f) | near_mid16(h) |
+         (tiny32(h) & (gu != 0.0f));
 }
 
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {   // RNE, two values
@@ -168,18 +171,20 @@ __device__ __noinline__ uint32_t rms_slow(float xf, float gf, double r) {
   return f64_to_bf16(h, [](double, double d) { return d; });  // fp64 decides
 }
 
-// Elements the fast value (x * r32 * gamma, within 3 fp32 ulps of the real
-// value) cannot decide: near a bf16 rounding midpoint, or tiny while x and
-// gamma are not zero.
-__device__ __forceinline__ bool rms_flag(float x, float gm, float h) {
-  return near_mid16(h) | (tiny32(h) & (x != 0.0f) & (gm != 0.0f));
+// Elements the fast value (t = x * r32, then h = t * gamma: within 3 fp32
+// ulps of the real value while both stay normal) cannot decide: h near a
+// bf16 rounding midpoint, or t or h tiny while x and gamma are not zero (a
+// t in fp32's subnormal range has lost bits that a large gamma would carry
+// into a normal h).
+__device__ __forceinline__ bool rms_flag(float x, float gm, float t, float h) {
+  return near_mid16(h) | ((tiny32(t) | tiny32(h)) & (x != 0.0f) & (gm != 0.0f));
 }
 
 // 8 values and their 8 gamma entries -> 8 normalized values (bf16).
 __device__ __forceinline__ uint4 rms8(uint4 xv, uint4 gv, float r32, double r64) {
   const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
   const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-  float x[8], gm[8], h[8];
+  float x[8], gm[8], t[8], h[8];
   bool any = false;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -190,8 +195,9 @@ __device__ __forceinline__ uint4 rms8(uint4 xv, uint4 gv, float r32, double r64)
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    h[i] = x[i] * r32 * gm[i];
-    any |= rms_flag(x[i], gm[i], h[i]);
+    t[i] = x[i] * r32;
+    h[i] = t[i] * gm[i];
+    any |= rms_flag(x[i], gm[i], t[i], h[i]);
   }
   uint32_t o[4];
 #pragma unroll
@@ -199,7 +205,7 @@ __device__ __forceinline__ uint4 rms8(uint4 xv, uint4 gv, float r32, double r64)
   if (__builtin_expect(any, 0)) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (rms_flag(x[i], gm[i], h[i])) {
+      if (rms_flag(x[i], gm[i], t[i], h[i])) {
         const uint32_t b = rms_slow(x[i], gm[i], r64);
         o[i >> 1] = (i & 1) ? ((o[i >> 1] & 0xFFFFu) | (b << 16)) : ((o[i >> 1] & 0xFFFF0000u) | b);
       }
@@ -550,15 +556,19 @@ __global__ __launch_bounds__(TW >= 4 ? 64 * TW : 256) void kv_quant_kernel(
   uint2* cache = is_v ? vc : kc;
   float* cscale = is_v ? vs : ks;
   const int64_t nch = width >> 3;
-  const int64_t slot = t < T ? slots[t] : -1;
-  const bool row_ok = slot >= 0 && slot < n_slots;   // out-of-range slots are skipped
-  const uint4* xr = x + (t < T ? t : 0) * nch;
+  const bool tok = t < T;
+  // the row's loads do not wait for its slot: they go out together with the
+  // slot's load, and the slot only decides the store (rows of skipped slots
+  // are read and dropped)
+  const int64_t slot = tok ? slots[t] : -1;
+  const uint4* xr = x + (tok ? t : 0) * nch;
   uint4 h[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int64_t c = (int64_t)i * TEAM + tl;
-    h[i] = ld16_if(xr, c, row_ok && c < nch);
+    h[i] = ld16_if<true>(xr, c, tok && c < nch);
   }
+  const bool row_ok = slot >= 0 && slot < n_slots;   // out-of-range slots are skipped
   quantize_team<CH, TW>(h, row_ok, row_ok ? slot : 0, nch, tl, red, cache, cscale);
 }
 

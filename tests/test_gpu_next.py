@@ -357,3 +357,74 @@ def test_silu_structural_ties(F):
     qo, so = O.silu_mul_quant(gu)
     assert_scales_equal(s.cpu().numpy(), so, "structural tie scales")
     assert_codes_equal(q.cpu().numpy(), qo, "structural tie codes")
+
+
+def silu_big_products(rows, inner, seed):
+    """Gates with |g| <= 64 beside ups near the bf16 maximum, so that g*u
+    passes 2^128 (fp32 overflow) while h = silu(g) * u stays a finite bf16:
+    g in [1.06, 1.3] (silu(g) <= 1.03) or in [-60, -1.06] (|silu(g)| < 0.28)
+    against |u| in [1.5, 1.9] * 2^127; the other half of the columns ordinary."""
+    rng = np.random.default_rng(seed)
+    g = np.where(rng.random((rows, inner)) < 0.5, rng.uniform(1.06, 1.3, (rows, inner)),
+                 -rng.uniform(1.06, 60.0, (rows, inner)))
+    u = rng.choice([-1.0, 1.0], (rows, inner)) * rng.uniform(1.5, 1.9, (rows, inner)) * 2.0 ** 127
+    plain = rng.random((rows, inner)) < 0.5
+    g = np.where(plain, rng.normal(0.0, 2.0, (rows, inner)), g)
+    u = np.where(plain, rng.normal(0.0, 1.0, (rows, inner)), u)
+    return np.concatenate([bits_of(g), bits_of(u)], axis=1)
+
+
+def test_silu_mul_fp32_overflowing_products(F):
+    """Elements whose fp32 product g*u overflows while h is finite take the
+    exact path: bf16 h and codes bit-exact."""
+    gu = silu_big_products(16, 1024, 4242)
+    want = O.silu_mul_bf16(gu)
+    assert not np.any((want & 0x7F80) == 0x7F80), "test data must keep h finite"
+    g = synth.bf16_bits_to_f32(gu[:, :1024]).astype(np.float32)
+    u = synth.bf16_bits_to_f32(gu[:, 1024:]).astype(np.float32)
+    with np.errstate(over="ignore"):
+        assert np.count_nonzero(np.isinf(g * u)) > 1000, "g*u must overflow fp32"
+    say(f"silu_mul fp32-overflowing g*u {gu.shape}")
+    h = F.fp8_silu_mul(dev_bf16(gu))
+    q, s = F.fp8_silu_mul_quant(dev_bf16(gu))
+    torch.cuda.synchronize()
+    got = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    bad = np.flatnonzero(got.ravel() != want.ravel())
+    assert bad.size == 0, f"{bad.size} h mismatches, first at {bad[:5]}"
+    qo, so = O.silu_mul_quant(gu)
+    assert_scales_equal(s.cpu().numpy(), so, "overflowing-product scales")
+    assert_codes_equal(q.cpu().numpy(), qo, "overflowing-product codes")
+
+
+def rms_tiny_products(rows, hidden, seed):
+    """Rows whose RMS is 1 to 2^23 (r = 1/RMS down to 2^-23) holding, in half
+    of the columns, bf16-subnormal x (down to 2^-133) under gammas of 2^100 to
+    2^127: x * r falls into (or below) fp32's subnormal range while
+    gamma * x * r is an ordinary normal value (the other columns' gammas are
+    scaled by 2^-40, so these values also decide the scales and codes)."""
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0.0, 1.0, (rows, hidden)) * 2.0 ** rng.integers(0, 24, (rows, 1))
+    gamma = rng.normal(1.0, 0.3, hidden) * 2.0 ** -40   # so the tiny-x columns set the amax
+    cols = rng.random(hidden) < 0.5
+    sub = rng.integers(1, 128, (rows, hidden)) * 2.0 ** -133 * rng.choice([-1.0, 1.0], (rows, hidden))
+    x = np.where(cols[None, :], sub, x)
+    gamma = np.where(cols, rng.choice([2.0 ** 100, 1.5 * 2.0 ** 110, 2.0 ** 120, 1.75 * 2.0 ** 126],
+                                      hidden), gamma)
+    return bits_of(x), bits_of(gamma)
+
+
+def test_rmsnorm_subnormal_intermediate(F):
+    """x * r in fp32's subnormal range under a large gamma takes the exact
+    path: bf16 h and codes bit-exact."""
+    x, gamma = rms_tiny_products(16, 1024, 4343)
+    say(f"rmsnorm subnormal x*r {x.shape}")
+    want = O.rmsnorm_bf16(x, gamma)
+    h = F.fp8_rmsnorm(dev_bf16(x), dev_bf16(gamma))
+    q, s = F.fp8_rmsnorm_quant(dev_bf16(x), dev_bf16(gamma))
+    torch.cuda.synchronize()
+    got = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    bad = np.flatnonzero(got.ravel() != want.ravel())
+    assert bad.size == 0, f"{bad.size} h mismatches, first at {bad[:5]}"
+    qo, so = O.rmsnorm_quant(x, gamma)
+    assert_scales_equal(s.cpu().numpy(), so, "subnormal-intermediate scales")
+    assert_codes_equal(q.cpu().numpy(), qo, "subnormal-intermediate codes")
