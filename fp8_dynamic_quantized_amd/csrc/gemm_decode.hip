@@ -114,8 +114,9 @@ __device__ __forceinline__ v4f ld_part(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kSc1));
 }
 
-// y[m, n..n+3] = bf16(v * scales) (per-channel: sx[m] * sw[n+r]; block: v is
-// already scaled); columns past N are not written.
+// y[m, n..n+3] = bf16(v * scales) (per-channel: v * (sx[m] * sw[n+r]), the
+// scale product first, since v * sx[m] alone could pass fp32's range while y
+// stays finite; block: v is already scaled); columns past N are not written.
 template <bool BLOCK>
 __device__ __forceinline__ void store_out(uint16_t* __restrict__ y, const float* __restrict__ sx,
                                           const float* __restrict__ sw, int m, int n, int N,
@@ -123,7 +124,7 @@ __device__ __forceinline__ void store_out(uint16_t* __restrict__ y, const float*
   float v[4];
   const float sm = BLOCK ? 1.0f : sx[m];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) v[r] = BLOCK ? s[r] : s[r] * sm * sw[min(n + r, N - 1)];
+  for (int r = 0; r < 4; ++r) v[r] = BLOCK ? s[r] : s[r] * (sm * sw[min(n + r, N - 1)]);
   uint16_t* out = y + (int64_t)m * N + n;
   if ((N & 3) == 0 && n + 3 < N) {
     uint2 pk;

@@ -533,8 +533,10 @@ __global__ __launch_bounds__((64 * LineCfg<BLOCK, BNP>::NW), 1) void gemm_prefil
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int q = 2 * qp + u;
-        w[u][0] = pk_bf16_rne(acc[i][j][4 * q + 0] * sm * s4[q].x, acc[i][j][4 * q + 1] * sm * s4[q].y);
-        w[u][1] = pk_bf16_rne(acc[i][j][4 * q + 2] * sm * s4[q].z, acc[i][j][4 * q + 3] * sm * s4[q].w);
+        // the scale product first: acc * sx alone could pass fp32's range
+        // (activation rows near the bf16 maximum) while y stays finite
+        w[u][0] = pk_bf16_rne(acc[i][j][4 * q + 0] * (sm * s4[q].x), acc[i][j][4 * q + 1] * (sm * s4[q].y));
+        w[u][1] = pk_bf16_rne(acc[i][j][4 * q + 2] * (sm * s4[q].z), acc[i][j][4 * q + 3] * (sm * s4[q].w));
       }
       // lane l (kh 0) keeps its q = 2qp values and takes lane l+32's; lane
       // l+32 keeps its q = 2qp+1 values and takes lane l's

@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
           for (int r = 0; r < 4; ++r) s4[r] = (n + r < N) ? sw[n + r] : 0.f;
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][r] * sm * s4[r];
+        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][r] * (sm * s4[r]);   // scales first
       }
       uint16_t* out = y + (int64_t)m * N + n;
       if (vec_ok && n + 3 < N) {

@@ -10,6 +10,8 @@ measured accumulation law of the FP8 matrix instructions (tests/mfma_law.py).
   law's prediction (and the nominal tolerance counted).
 * Every output of the 70B decode o and down linears at 1 and 64 tokens
   within the tolerance of the oracle.
+* Per-channel scales near both ends of the fp32 range on every kernel path:
+  finite outputs, within the tolerance of the law's prediction.
 """
 import numpy as np
 import pytest
@@ -220,3 +222,59 @@ def test_c3_every_output(F, j):
         ref = (O.e4m3_decode(qx_o) @ vw.T) * sx_o.astype(np.float64)[:, None] \
             * sw_o.astype(np.float64)[None, :]
         assert_y_close(host_bf16_f64(y), ref, f"M={M}")
+
+
+def _sample(n, k, seed):
+    """The first and last 16 indices and k random ones, sorted, unique."""
+    rng = np.random.default_rng(seed)
+    edge = min(16, n)
+    idx = np.concatenate([np.arange(edge), np.arange(n - edge, n),
+                          rng.choice(n, size=min(k, n), replace=False)])
+    return np.unique(idx)
+
+
+@pytest.mark.parametrize("M,N,K,flags", [(4096, 4096, 1024, 1), (4096, 6144, 512, 1),
+                                         (512, 512, 1024, 1), (512, 512, 128, 1),
+                                         (3, 512, 1024, 2), (16, 512, 1024, 2),
+                                         (64, 512, 1024, 2)],
+                         ids=["wide_tiles", "tiles_192", "small_tiles", "k128", "decode_3_rows",
+                              "decode_16_rows", "decode_64_rows"])
+def test_per_channel_scale_extremes(F, M, N, K, flags):
+    """Per-channel scales near both ends of the fp32 range: activation rows
+    scaled by 2^90 to 2^118 (so acc * sx alone passes 2^128 while y stays
+    finite) and by 2^-110 and 2^-120, weight rows by 2^-20 to 2^0. Every
+    kernel path (256 x 256 and 256 x 192 whole-line tiles, the small-tile
+    kernel and its K = 128 case, the register and whole-line decode kernels)
+    gives finite outputs within tolerance of the matrix instruction's
+    accumulation law (tests/mfma_law.py) times the scales, on sampled rows
+    and columns. (Against the exact sum, the rows scaled up lose the
+    absolute term of the tolerance that covers cancelling sums near zero,
+    so the law's cut shows as a relative error there.)"""
+    say(f"per-channel scale extremes {M}x{N}x{K} flags={flags}")
+    rng = np.random.default_rng(M + N + K)
+    xf = synth.bf16_bits_to_f32(synth.activations(M, K, 3400 + M, 3401)).astype(np.float64)
+    ex = np.array([0, 90, 100, 110, 114, 118, -110, -120])[(5 + 3 * np.arange(M)) % 8]
+    xb = synth.f32_to_bf16_bits((xf * 2.0 ** ex[:, None]).astype(np.float32))
+    wf = synth.bf16_bits_to_f32(synth.weights(N, K, 3402 + N)).astype(np.float64)
+    ew = rng.choice([-20, -10, -4, 0], N)
+    wb = synth.f32_to_bf16_bits((wf * 2.0 ** ew[:, None]).astype(np.float32))
+    qx, sx = O.quant_per_row(xb)
+    qw, sw = O.quant_per_row(wb)
+    rows = np.unique(np.concatenate([np.arange(min(16, M)), _sample(M, 48, 41)]))
+    cols = np.unique(np.concatenate([np.arange(8), _sample(N, 40, 42)]))
+    acc = O.gemm_codes(qx[rows], qw[cols])
+    ref = O.linear_per_channel(qx[rows], sx[rows], qw[cols], sw[cols])
+    assert np.all(np.abs(ref) < 2.0 ** 127), "test data must keep y finite in bf16"
+    vx, vw = O.e4m3_decode(qx[rows]), O.e4m3_decode(qw[cols])
+    law = law_sum_split(vx, vw) if flags == 2 else law_sum(vx, vw)
+    pred = law * (sx[rows].astype(np.float64)[:, None] * sw[cols].astype(np.float64)[None, :])
+    with np.errstate(over="ignore"):
+        assert np.any(np.isinf(acc.astype(np.float32) * sx[rows, None])), \
+            "the case must take acc * sx past fp32's range"
+    y = F.fp8_gemm(dev(qx), dev(sx), dev(qw), dev(sw), flags=flags)
+    torch.cuda.synchronize()
+    got = host_bf16_f64(y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
+    assert np.all(np.isfinite(got)), "non-finite outputs"
+    assert_y_close(got, pred, "y against the law")
+    off = ~O.within_tolerance(got, ref)
+    say(f"  {off.sum()} of {off.size} sampled outputs outside the tolerance of the exact sum")
