@@ -495,7 +495,7 @@ def copy_calibration(torch):
 
 
 PROFILE_REPS = {"copy": (0, 3), "decode": (4, 8), "quant": (4, 8), "prefill": (2, 4),
-                "block": (2, 4)}
+                "block": (2, 4), "groupquant": (4, 8), "next": (4, 8)}
 
 
 def profile_case(case, out_dir, torch):
@@ -549,6 +549,74 @@ def profile_case(case, out_dir, torch):
         kernels.append({"match": "quant_rows", "bytes": 3 * M * K + 4 * M, "read": 2 * M * K,
                         "write": M * K + 4 * M, "flops": 0,
                         "what": f"per-token quantizer {M}x{K} read cold: x 2MK, codes MK, scales 4M"})
+    elif kind == "groupquant":
+        # the block variant's activation quantizer (128-wide groups) on the
+        # Llama-3.2-3B inputs, rotated over > 1 GB so it reads from HBM
+        _, ms, ks = case.split(":")
+        M, K = int(ms), int(ks)
+        copies = max(2, -(-(1 << 30) // (2 * M * K)) + 1)
+        xs = [to_dev(synth.activations(M, K, 11 + c, 12), torch) for c in range(min(copies, 3))]
+        xs += [xs[c % 3].clone() for c in range(3, copies)]
+        q = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+        run = lambda i: F.fp8_quant_act(xs[i % copies], group=128, q=q, scale=sc)   # noqa: E731
+        kernels.append({"match": "quant_groups", "bytes": 3 * M * K + 4 * M * K // 128,
+                        "read": 2 * M * K, "write": M * K + 4 * M * K // 128, "flops": 0,
+                        "what": f"group-128 quantizer {M}x{K} read cold: x 2MK, codes MK, "
+                                f"scales 4MK/128"})
+    elif kind == "next":
+        # the fused producers, static quantization, calibration and KV-cache
+        # write at the sizes bench.py times (inputs resident, as there)
+        _, row = case.split(":")
+        M, inner, hidden = 4096, 14336, 4096
+        if row == "silu":
+            gu = to_dev(synth.activations(M, 2 * inner, 61, 62), torch)
+            q = torch.empty((M, inner), dtype=torch.uint8, device="cuda")
+            s = torch.empty((M,), dtype=torch.float32, device="cuda")
+            run = lambda i: F.fp8_silu_mul_quant(gu, q=q, scale=s)   # noqa: E731
+            rd, wr = M * 2 * inner * 2, M * inner + 4 * M
+            match, what = "silu_mul_kernel", f"SwiGLU -> FP8: gate_up out [{M},{2 * inner}] bf16 in, codes [{M},{inner}] + scales out"
+        elif row == "rms":
+            x = to_dev(synth.activations(M, hidden, 63, 64), torch)
+            gamma = torch.ones(hidden, dtype=torch.bfloat16, device="cuda")
+            q = torch.empty((M, hidden), dtype=torch.uint8, device="cuda")
+            s = torch.empty((M,), dtype=torch.float32, device="cuda")
+            run = lambda i: F.fp8_rmsnorm_quant(x, gamma, q=q, scale=s)   # noqa: E731
+            rd, wr = M * hidden * 2 + hidden * 2, M * hidden + 4 * M
+            match, what = "rmsnorm_kernel", f"RMSNorm -> FP8: x [{M},{hidden}] + gamma in, codes + scales out"
+        elif row == "static":
+            x = to_dev(synth.activations(M, hidden, 63, 64), torch)
+            s = torch.full((1,), 0.01, dtype=torch.float32, device="cuda")
+            q = torch.empty((M, hidden), dtype=torch.uint8, device="cuda")
+            run = lambda i: F.fp8_quant_static(x, s, q=q)   # noqa: E731
+            rd, wr = M * hidden * 2 + 4, M * hidden
+            match, what = "quant_static_kernel", f"static quantization [{M},{hidden}]: x in, codes out"
+        elif row == "kv":
+            T, width, n_slots = 4096, 8 * 128, 8192
+            k = to_dev(synth.activations(T, width, 65, 66), torch)
+            v = to_dev(synth.activations(T, width, 67, 68), torch)
+            slots = torch.randperm(n_slots, generator=torch.Generator().manual_seed(69))[:T].cuda()
+            kc = torch.empty((n_slots, width), dtype=torch.uint8, device="cuda")
+            vc = torch.empty_like(kc)
+            ks = torch.empty((n_slots,), dtype=torch.float32, device="cuda")
+            vs = torch.empty_like(ks)
+            run = lambda i: F.fp8_kv_cache_quant(k, v, slots, kc, vc, ks, vs)   # noqa: E731
+            rd, wr = 2 * T * width * 2 + 8 * T, 2 * (T * width + 4 * T)
+            match, what = "kv_quant_kernel", f"FP8 KV-cache write: K, V [{T},{width}] + slots in, cache rows + scales out"
+        elif row == "calib":
+            n = 64 * 2048 * hidden     # 2^29 values (the bench runs 8 times as many)
+            g = torch.Generator(device="cuda")
+            g.manual_seed(synth.seed_of(6, 0, 0, 0))
+            cal = torch.randn((64 * 2048, hidden), generator=g, device="cuda").to(torch.bfloat16)
+            s = torch.empty((1,), dtype=torch.float32, device="cuda")
+            ws = torch.empty(F.fp8_calib_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+            run = lambda i: F.fp8_calib_scale(cal, 1, 999, scale=s, ws=ws)   # noqa: E731
+            rd, wr = 2 * n, 0
+            match, what = "calib_hist_kernel", f"calibration histogram pass over {n} bf16 values (two per call)"
+        else:
+            raise SystemExit(f"unknown next-row case {row}")
+        kernels.append({"match": match, "bytes": rd + wr, "read": rd, "write": wr, "flops": 0,
+                        "what": what})
     elif kind in ("prefill", "block"):
         _, lin = case.split(":")
         c = 2 if kind == "prefill" else 4

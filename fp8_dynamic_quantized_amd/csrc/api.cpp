@@ -241,7 +241,9 @@ int fp8_rmsnorm_quant(const void* x_bf16, const void* gamma_bf16, int64_t rows, 
                       double eps, uint8_t* q, float* scale, void* stream) {
   if (rows < 0 || H <= 0 || (H % 8) != 0 || H > kMaxFusedRow) return FP8DQ_ERR_SHAPE;
   if (rows > INT32_MAX) return FP8DQ_ERR_SHAPE;
-  if (!(eps >= 0.0) || eps > 1.0e30) return FP8DQ_ERR_SHAPE;  // NaN fails too
+  // eps in [1e-30, 1e30] (NaN fails too): 1 / sqrt(mean + eps) then stays
+  // below 1e15, inside fp32's range, whatever the row
+  if (!(eps >= 1.0e-30) || eps > 1.0e30) return FP8DQ_ERR_SHAPE;
   if (rows == 0) return FP8DQ_OK;
   if (!x_bf16 || !gamma_bf16 || !q || !scale) return FP8DQ_ERR_NULL;
   if (!aligned16(x_bf16) || !aligned16(gamma_bf16) || !aligned16(q) || !aligned16(scale))
@@ -267,7 +269,7 @@ int fp8_rmsnorm(const void* x_bf16, const void* gamma_bf16, int64_t rows, int64_
                 void* h_bf16, void* stream) {
   if (rows < 0 || H <= 0 || (H % 8) != 0 || H > kMaxFusedRow) return FP8DQ_ERR_SHAPE;
   if (rows > INT32_MAX) return FP8DQ_ERR_SHAPE;
-  if (!(eps >= 0.0) || eps > 1.0e30) return FP8DQ_ERR_SHAPE;
+  if (!(eps >= 1.0e-30) || eps > 1.0e30) return FP8DQ_ERR_SHAPE;   // as fp8_rmsnorm_quant
   if (rows == 0) return FP8DQ_OK;
   if (!x_bf16 || !gamma_bf16 || !h_bf16) return FP8DQ_ERR_NULL;
   if (!aligned16(x_bf16) || !aligned16(gamma_bf16) || !aligned16(h_bf16)) return FP8DQ_ERR_ALIGN;

@@ -258,7 +258,9 @@ int fp8_silu_mul_quant(const void* gu_bf16, int64_t rows, int64_t I, uint8_t* q,
  *   h[r,i] = bf16( gamma[i] * x[r,i] / sqrt(mean_i(x[r,i]^2) + eps) ),
  *   x bf16 [rows, H], gamma bf16 [H]; q [rows, H], scale [rows].
  * Source: §1.3 of the page (eps = 1e-5, norm before attention and the MLP;
- * §5.3 keeps the norm itself in bf16). eps >= 0 (FP8DQ_ERR_SHAPE otherwise).
+ * §5.3 keeps the norm itself in bf16). 1e-30 <= eps <= 1e30 (FP8DQ_ERR_SHAPE
+ * otherwise): 1 / sqrt(mean + eps) then stays inside fp32's range (with
+ * eps = 0 an all-zero row would have no value).
  * Size rules: rows >= 0; H > 0, H % 8 == 0, H <= 65536.
  */
 int fp8_rmsnorm_quant(const void* x_bf16, const void* gamma_bf16, int64_t rows, int64_t H,

@@ -148,6 +148,9 @@ def test_fused_producer_errors(L):
     assert g(A, None, 4, 256, 1e-5, A, A, None) == -1
     assert g(A, A, 4, 12, 1e-5, A, A, None) == -2
     assert g(A, A, 4, 256, -1.0, A, A, None) == -2    # negative eps
+    assert g(A, A, 4, 256, 0.0, A, A, None) == -2     # eps below 1e-30
+    assert g(A, A, 4, 256, 1e-31, A, A, None) == -2
+    assert g(A, A, 4, 256, 1e31, A, A, None) == -2
     assert g(A, A, 4, 256, float("nan"), A, A, None) == -2
     assert g(A, MIS, 4, 256, 1e-5, A, A, None) == -3
     assert g(None, None, 0, 256, 1e-5, None, None, None) == 0
@@ -161,6 +164,7 @@ def test_fused_producer_errors(L):
     assert g(A, A, 4, 256, 1e-5, None, None) == -1
     assert g(A, A, 4, 12, 1e-5, A, None) == -2
     assert g(A, A, 4, 256, -1.0, A, None) == -2
+    assert g(A, A, 4, 256, 0.0, A, None) == -2
     assert g(A, A, 4, 256, 1e-5, MIS, None) == -3
     assert g(None, None, 0, 256, 1e-5, None, None) == 0
 
