@@ -310,7 +310,9 @@ int fp8_quant_static(const void* x_bf16, int64_t n, const float* scale, uint8_t*
  * in fp8_quant_act and stored in cache row slots[t] of k_cache / v_cache
  * (uint8 [n_slots, width]) with its scale in k_scale / v_scale (fp32
  * [n_slots]); tokens whose slot is negative or >= n_slots are not written.
- * slots: device int64 [T]. Source: §4.1 of the page (FP8 also compresses
+ * Valid slots are expected to be distinct (as a cache's slot mapping is):
+ * when two tokens name one slot, which token's row and scale the slot ends
+ * up holding is unspecified. slots: device int64 [T]. Source: §4.1 of the page (FP8 also compresses
  * the KV cache). Size rules: T >= 0; width > 0, width % 8 == 0,
  * width <= 65536; n_slots >= 0.
  */
