@@ -612,7 +612,8 @@ def profile_case(case, out_dir, torch):
             ws = torch.empty(F.fp8_calib_workspace_bytes(n), dtype=torch.uint8, device="cuda")
             run = lambda i: F.fp8_calib_scale(cal, 1, 999, scale=s, ws=ws)   # noqa: E731
             rd, wr = 2 * n, 0
-            match, what = "calib_hist_kernel", f"calibration histogram pass over {n} bf16 values (two per call)"
+            match, what = "calib_hist_kernel", (f"calibration histogram pass over {n} bf16 values "
+                                                f"(two per call; the histograms are workspace)")
         else:
             raise SystemExit(f"unknown next-row case {row}")
         kernels.append({"match": match, "bytes": rd + wr, "read": rd, "write": wr, "flops": 0,
@@ -791,7 +792,8 @@ def summarize_profile(dirs):
                     if rd is not None:
                         parts.append(f"read {rd / 1e6:.3f} MB ({rd / k['read']:.2f}x)")
                     if wr is not None:
-                        parts.append(f"write {wr / 1e6:.3f} MB ({wr / max(k['write'], 1):.2f}x)")
+                        parts.append(f"write {wr / 1e6:.3f} MB ({wr / k['write']:.2f}x)" if k["write"]
+                                     else f"write {wr / 1e6:.3f} MB (no algorithmic output)")
                     if rd is not None and wr is not None:
                         parts.append(f"total {(rd + wr) / 1e6:.3f} MB ({(rd + wr) / alg:.2f}x)")
                         if avg_us:
