@@ -25,6 +25,9 @@
  *           code, saturating at +-448, sign of zero kept); q = +-0 if s = 0
  *   y     = bf16_RNE( sum_k val(qx[m,k]) val(qw[n,k]) * sx[m] * sw[n] )
  *   block: y = bf16_RNE( sum_g (sum_{k in g} val*val) * sx[m,g] * sw[n/128,g] )
+ *   The scale product sx * sw (per channel, or per group) is formed first,
+ *   so every intermediate stays inside fp32 while that product is below
+ *   2^128 (both amax beyond about 2^73 at once is outside this range).
  *   The sum is accumulated in fp32 (any order); codes and scales are
  *   bit-exact. y is within 1e-2 relative / 1e-3 absolute of the exact value
  *   on the decode path; the prefill path is exact to the matrix
