@@ -226,10 +226,31 @@ __device__ __forceinline__ double chunk_sumsq(uint4 v) {
   return s;
 }
 
+// Sum over the wave's 64 lanes, in every lane, by the same lane pairings
+// as wave64_max (both 32-bit halves of each value moved); the pairs add in
+// either order to the same bits, so every lane ends with one value.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = dpp_mov<CTRL>((uint32_t)b), hi = dpp_mov<CTRL>((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+__device__ __forceinline__ double join_f64(uint32_t lo, uint32_t hi) {
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  v += dpp_f64<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141>(v);   // row_half_mirror
+  v += dpp_f64<0x140>(v);   // row_mirror
+  uint64_t b = (uint64_t)__double_as_longlong(v);
+  const auto l16 = __builtin_amdgcn_permlane16_swap((uint32_t)b, (uint32_t)b, false, false);
+  const auto h16 = __builtin_amdgcn_permlane16_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+  v = join_f64(l16[0], h16[0]) + join_f64(l16[1], h16[1]);
+  b = (uint64_t)__double_as_longlong(v);
+  const auto l32 = __builtin_amdgcn_permlane32_swap((uint32_t)b, (uint32_t)b, false, false);
+  const auto h32 = __builtin_amdgcn_permlane32_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+  return join_f64(l32[0], h32[0]) + join_f64(l32[1], h32[1]);
 }
 
 // ---- shared per-row tail: amax of the h chunks, scale, codes ---------------
@@ -247,7 +268,7 @@ __device__ __forceinline__ void quantize_team(const uint4 (&h)[CH], bool row_ok,
     if ((int64_t)i * TEAM + team_lane < nch) m2 = a;
   }
   uint32_t m = m2.x > m2.y ? m2.x : m2.y;
-  m = wave_max_u32(m);
+  m = wave64_max(m);
   if (TW > 1) {   // the team's waves meet in red[team * TW ...]
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();

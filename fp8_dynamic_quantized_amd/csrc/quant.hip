@@ -73,7 +73,7 @@ __global__ __launch_bounds__(TEAM_WAVES >= 4 ? 64 * TEAM_WAVES : 256) void quant
 #pragma unroll
   for (int i = 0; i < CH; ++i) m2 = chunk_amax(v[i], m2);
   uint32_t m = m2.x > m2.y ? m2.x : m2.y;
-  m = wave_max_u32(m);
+  m = wave64_max(m);
   if (TEAM_WAVES > 1) {   // the team's waves meet in red[team * TEAM_WAVES ...]
     if ((tid & 63) == 0) red[tid >> 6] = m;
     __syncthreads();
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void quant_rows_2pass_kernel(
   us2 m2 = {0, 0};
   for (int64_t c = tid; c < nch; c += 256) m2 = chunk_amax(xr[c], m2);
   uint32_t m = m2.x > m2.y ? m2.x : m2.y;
-  m = wave_max_u32(m);
+  m = wave64_max(m);
   if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
   m = red[0];
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void quant_groups_kernel(
     const int64_t c = base + (int64_t)u * 256;
     us2 m2 = chunk_amax(v[u], us2{0, 0});
     uint32_t m = m2.x > m2.y ? m2.x : m2.y;
-    m = group_max_u32<16>(m);
+    m = row16_max(m);
     float s, r, p;
     bool tiny;
     unit_scale(m, s, r, p, tiny);
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void quant_wblock_kernel(
     m2 = chunk_amax(v[i], m2);
   }
   uint32_t m = m2.x > m2.y ? m2.x : m2.y;
-  m = wave_max_u32(m);
+  m = wave64_max(m);
   if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
   m = red[0];

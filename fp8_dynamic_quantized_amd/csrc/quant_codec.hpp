@@ -104,6 +104,37 @@ __device__ __forceinline__ us2 chunk_amax(uint4 v, us2 acc) {
   return acc;
 }
 
+// Lane reductions without LDS, for a unit's amax: DPP moves inside rows of
+// 16 lanes (swap neighbours, swap pairs, half-row mirror, row mirror: after
+// each step a quad, an 8-lane half-row, then the row hold one value), then
+// v_permlane16_swap (rows 0 and 1, 2 and 3) and v_permlane32_swap (the two
+// halves). Each step pairs lanes, so every lane ends with the same value.
+// All 64 lanes must be active. (The lane shuffles these replace went through
+// ds_bpermute, an LDS round trip per step, on the row's critical chain.)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// maximum over each row of 16 lanes, in every lane of the row
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = umax32(v, dpp_mov<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = umax32(v, dpp_mov<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = umax32(v, dpp_mov<0x141>(v));   // row_half_mirror
+  v = umax32(v, dpp_mov<0x140>(v));   // row_mirror
+  return v;
+}
+
+// maximum over the wave's 64 lanes, in every lane
+__device__ __forceinline__ uint32_t wave64_max(uint32_t v) {
+  v = row16_max(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = umax32(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return umax32(b[0], b[1]);
+}
+
 __device__ __forceinline__ void unit_scale(uint32_t amax_bits, float& s,
                                            float& r, float& p, bool& tiny) {
   float amax = __uint_as_float(amax_bits << 16);
