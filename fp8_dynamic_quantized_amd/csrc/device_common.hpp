@@ -71,27 +71,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
-// Wave-wide (64 lanes) maximum of an unsigned value.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t o = __shfl_xor(v, off, 64);
-    v = v > o ? v : o;
-  }
-  return v;
-}
-
-// Maximum over aligned groups of `width` lanes (width a power of two <= 64).
-template <int width>
-__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = width / 2; off >= 1; off >>= 1) {
-    uint32_t o = __shfl_xor(v, off, 64);
-    v = v > o ? v : o;
-  }
-  return v;
-}
-
 
 // LDS (address space 3) pointer, for taking the 32-bit LDS address of a
 // shared array.
