@@ -74,6 +74,7 @@ KERNEL_SOURCES = ["fp8_dynamic_quantized_amd/csrc/gemm_line.hpp",
                   "fp8_dynamic_quantized_amd/csrc/gemm_prefill.hip",
                   "fp8_dynamic_quantized_amd/csrc/device_common.hpp"]
 COPY_BYTES = 1 << 30
+PER_LINEAR_STEPS = 20       # steps of the per-linear pass (events around every launch)
 
 
 def log(*a):
@@ -202,7 +203,7 @@ def bench_prefill(F, torch, steps, warmup, only=None):
     dom_ms = np.mean([evs[k][dom][1].elapsed_time(evs[k][dom][2]) for k in range(steps)])
 
     # per-linear breakdown: a separate pass, events around every launch
-    diag = max(5, min(steps, 20))
+    diag = max(5, min(steps, PER_LINEAR_STEPS))
     evd = new_events(diag)
     for k in range(diag):
         step(evd[k], every=True)
@@ -714,6 +715,16 @@ def summarize_profile(dirs):
                     if len(gu) >= last:
                         print(f"# gate_up GEMM, mean of the last {last} launches: "
                               f"{np.mean(gu[-last:]):.2f} us")
+                # a default-protocol run ends with the per-linear pass of
+                # PER_LINEAR_STEPS steps; the launches before it are the
+                # warm-up and timed steps
+                if len(gu) >= 2 * PER_LINEAR_STEPS:
+                    timed = gu[-2 * PER_LINEAR_STEPS:-PER_LINEAR_STEPS]
+                    print(f"# gate_up GEMM, mean of the {PER_LINEAR_STEPS} launches before the "
+                          f"per-linear pass (the timed steps when --steps is "
+                          f"{PER_LINEAR_STEPS}): {np.mean(timed):.2f} us")
+                    print(f"# gate_up GEMM in the per-linear pass (events around every launch): "
+                          f"mean {np.mean(gu[-PER_LINEAR_STEPS:]):.2f} us")
             cagg = {}
             for did, cv in ctr.items():
                 for cn, v in cv.items():
