@@ -93,22 +93,50 @@ def _check(fn: str, status: int) -> None:
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: the argtypes (c_void_p) convert it, with no object per call
+    return None if t is None else t.data_ptr()
 
 
 def _stream(t, stream):
+    """The HIP stream to enqueue on: the one given, else torch's current
+    stream of t's device (read through torch's raw-stream accessor where it
+    has one: a small call matters when a decode linear takes 15 us)."""
     import torch
     if stream is not None:
-        return ctypes.c_void_p(stream)
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+        return stream
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(t.device.index)
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _need(t, dtype, shape, name):
-    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+def _need(t, dtype, shape, name, dev=None):
+    """Check one tensor argument before its pointer reaches the library: the
+    library sees only pointers and sizes, so a wrong shape, dtype, layout or
+    device here would become an out-of-bounds access on the GPU."""
+    if t is None:
+        raise ValueError(f"{name}: missing")
+    if t.dtype is not dtype or t.shape != tuple(shape) or not t.is_contiguous():
         raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)}, got "
                          f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
     if not t.is_cuda:
         raise ValueError(f"{name}: must be device memory")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name}: on {t.device}, the other operands on {dev}")
+
+
+def _need_ws(ws, dev):
+    """A caller's workspace: contiguous device memory on the operands' device
+    (its size is checked by the library)."""
+    if ws is None:
+        return
+    if not ws.is_contiguous() or not ws.is_cuda or ws.device != dev:
+        raise ValueError(f"ws: expected contiguous device memory on {dev}")
+
+
+def _need_blocks(N, K):
+    if N % GROUP or K % GROUP:
+        raise ValueError(f"block scales need N and K multiples of {GROUP}, got N={N}, K={K}")
 
 
 def fp8_workspace_bytes(M: int, N: int, K: int, block: bool = False,
@@ -129,9 +157,15 @@ def fp8_quant_act(x, group: int = 0, q=None, scale=None, stream=None):
     import torch
     rows, K = x.shape
     _need(x, torch.bfloat16, (rows, K), "x")
+    if group not in (0, GROUP):
+        raise ValueError(f"group: 0 or {GROUP}, got {group}")
+    if group and K % GROUP:
+        raise ValueError(f"group {GROUP} needs K a multiple of {GROUP}, got {K}")
     sshape = (rows,) if group == 0 else (rows, K // GROUP)
     q = torch.empty((rows, K), dtype=torch.uint8, device=x.device) if q is None else q
     scale = torch.empty(sshape, dtype=torch.float32, device=x.device) if scale is None else scale
+    _need(q, torch.uint8, (rows, K), "q", x.device)
+    _need(scale, torch.float32, sshape, "scale", x.device)
     _check("fp8_quant_act", lib().fp8_quant_act(
         _ptr(x), rows, K, group, _ptr(q), _ptr(scale), _stream(x, stream)))
     return q, scale
@@ -142,19 +176,25 @@ def fp8_quant_weight_block(w, qw=None, sw=None, stream=None):
     import torch
     N, K = w.shape
     _need(w, torch.bfloat16, (N, K), "w")
+    _need_blocks(N, K)
     qw = torch.empty((N, K), dtype=torch.uint8, device=w.device) if qw is None else qw
     sw = torch.empty((N // GROUP, K // GROUP), dtype=torch.float32,
                      device=w.device) if sw is None else sw
+    _need(qw, torch.uint8, (N, K), "qw", w.device)
+    _need(sw, torch.float32, (N // GROUP, K // GROUP), "sw", w.device)
     _check("fp8_quant_weight_block", lib().fp8_quant_weight_block(
         _ptr(w), N, K, _ptr(qw), _ptr(sw), _stream(w, stream)))
     return qw, sw
 
 
 def _workspace(M, N, K, block, flags, ws, device):
+    """The caller's workspace and its size in bytes, or a zero-filled one of
+    the size the call needs (the library checks the size either way)."""
     import torch
-    need = fp8_workspace_bytes(M, N, K, block, flags)
-    if need and ws is None:
-        ws = torch.zeros(need, dtype=torch.uint8, device=device)   # counters start at zero
+    if ws is None:
+        need = fp8_workspace_bytes(M, N, K, block, flags)
+        if need:
+            ws = torch.zeros(need, dtype=torch.uint8, device=device)   # counters start at zero
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     return ws, nbytes
 
@@ -164,8 +204,15 @@ def fp8_gemm(qx, sx, qw, sw, y=None, flags: int = AUTO, ws=None, stream=None):
     import torch
     M, K = qx.shape
     N = qw.shape[0]
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=qx.device) if y is None else y
-    ws, nb = _workspace(M, N, K, False, flags, ws, qx.device)
+    dev = qx.device
+    _need(qx, torch.uint8, (M, K), "qx", dev)
+    _need(sx, torch.float32, (M,), "sx", dev)
+    _need(qw, torch.uint8, (N, K), "qw", dev)
+    _need(sw, torch.float32, (N,), "sw", dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    _need(y, torch.bfloat16, (M, N), "y", dev)
+    _need_ws(ws, dev)
+    ws, nb = _workspace(M, N, K, False, flags, ws, dev)
     _check("fp8_gemm", lib().fp8_gemm(
         _ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(y), M, N, K, flags,
         _ptr(ws), nb, _stream(qx, stream)))
@@ -177,8 +224,16 @@ def fp8_gemm_block(qx, sx, qw, sw, y=None, flags: int = AUTO, ws=None, stream=No
     import torch
     M, K = qx.shape
     N = qw.shape[0]
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=qx.device) if y is None else y
-    ws, nb = _workspace(M, N, K, True, flags, ws, qx.device)
+    dev = qx.device
+    _need_blocks(N, K)
+    _need(qx, torch.uint8, (M, K), "qx", dev)
+    _need(sx, torch.float32, (M, K // GROUP), "sx", dev)
+    _need(qw, torch.uint8, (N, K), "qw", dev)
+    _need(sw, torch.float32, (N // GROUP, K // GROUP), "sw", dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    _need(y, torch.bfloat16, (M, N), "y", dev)
+    _need_ws(ws, dev)
+    ws, nb = _workspace(M, N, K, True, flags, ws, dev)
     _check("fp8_gemm_block", lib().fp8_gemm_block(
         _ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(y), M, N, K, flags,
         _ptr(ws), nb, _stream(qx, stream)))
@@ -199,6 +254,12 @@ def fp8_linear(x, qw, sw, y=None, qx_out=None, sx_out=None, flags: int = AUTO,
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
     qx_out = torch.empty((M, K), dtype=torch.uint8, device=dev) if qx_out is None else qx_out
     sx_out = torch.empty((M,), dtype=torch.float32, device=dev) if sx_out is None else sx_out
+    _need(qw, torch.uint8, (N, K), "qw", dev)
+    _need(sw, torch.float32, (N,), "sw", dev)
+    _need(y, torch.bfloat16, (M, N), "y", dev)
+    _need(qx_out, torch.uint8, (M, K), "qx_out", dev)
+    _need(sx_out, torch.float32, (M,), "sx_out", dev)
+    _need_ws(ws, dev)
     ws, nb = _workspace(M, N, K, False, flags, ws, dev)
     _check("fp8_linear", lib().fp8_linear(
         _ptr(x), _ptr(qw), _ptr(sw), _ptr(y), M, N, K, _ptr(qx_out), _ptr(sx_out),
@@ -221,6 +282,11 @@ def fp8_linear_noalloc(x, qw, sw, y=None, qx_out=None, sx_out=None, flags: int =
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
     qx_out = torch.empty((M, K), dtype=torch.uint8, device=dev) if qx_out is None else qx_out
     sx_out = torch.empty((M,), dtype=torch.float32, device=dev) if sx_out is None else sx_out
+    _need(qw, torch.uint8, (N, K), "qw", dev)
+    _need(sw, torch.float32, (N,), "sw", dev)
+    _need(y, torch.bfloat16, (M, N), "y", dev)
+    _need(qx_out, torch.uint8, (M, K), "qx_out", dev)
+    _need(sx_out, torch.float32, (M,), "sx_out", dev)
     _check("fp8_linear_noalloc", lib().fp8_linear_noalloc(
         _ptr(x), _ptr(qw), _ptr(sw), _ptr(y), M, N, K, _ptr(qx_out), _ptr(sx_out),
         flags, _stream(x, stream)))
@@ -237,11 +303,18 @@ def fp8_linear_block(x, qw, sw, y=None, qx_out=None, sx_out=None,
     M, K = x.shape
     N = qw.shape[0]
     _need(x, torch.bfloat16, (M, K), "x")
+    _need_blocks(N, K)
     dev = x.device
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
     qx_out = torch.empty((M, K), dtype=torch.uint8, device=dev) if qx_out is None else qx_out
     sx_out = (torch.empty((M, K // GROUP), dtype=torch.float32, device=dev)
               if sx_out is None else sx_out)
+    _need(qw, torch.uint8, (N, K), "qw", dev)
+    _need(sw, torch.float32, (N // GROUP, K // GROUP), "sw", dev)
+    _need(y, torch.bfloat16, (M, N), "y", dev)
+    _need(qx_out, torch.uint8, (M, K), "qx_out", dev)
+    _need(sx_out, torch.float32, (M, K // GROUP), "sx_out", dev)
+    _need_ws(ws, dev)
     ws, nb = _workspace(M, N, K, True, flags, ws, dev)
     _check("fp8_linear_block", lib().fp8_linear_block(
         _ptr(x), _ptr(qw), _ptr(sw), _ptr(y), M, N, K, _ptr(qx_out), _ptr(sx_out),
@@ -267,6 +340,8 @@ def fp8_silu_mul_quant(gu, q=None, scale=None, stream=None):
     inner = two_i // 2
     q = torch.empty((rows, inner), dtype=torch.uint8, device=gu.device) if q is None else q
     scale = torch.empty((rows,), dtype=torch.float32, device=gu.device) if scale is None else scale
+    _need(q, torch.uint8, (rows, inner), "q", gu.device)
+    _need(scale, torch.float32, (rows,), "scale", gu.device)
     _check("fp8_silu_mul_quant", lib().fp8_silu_mul_quant(
         _ptr(gu), rows, inner, _ptr(q), _ptr(scale), _stream(gu, stream)))
     return q, scale
@@ -278,9 +353,11 @@ def fp8_rmsnorm_quant(x, gamma, eps: float = RMS_EPS, q=None, scale=None, stream
     import torch
     rows, hidden = x.shape
     _need(x, torch.bfloat16, (rows, hidden), "x")
-    _need(gamma, torch.bfloat16, (hidden,), "gamma")
+    _need(gamma, torch.bfloat16, (hidden,), "gamma", x.device)
     q = torch.empty((rows, hidden), dtype=torch.uint8, device=x.device) if q is None else q
     scale = torch.empty((rows,), dtype=torch.float32, device=x.device) if scale is None else scale
+    _need(q, torch.uint8, (rows, hidden), "q", x.device)
+    _need(scale, torch.float32, (rows,), "scale", x.device)
     _check("fp8_rmsnorm_quant", lib().fp8_rmsnorm_quant(
         _ptr(x), _ptr(gamma), rows, hidden, float(eps), _ptr(q), _ptr(scale),
         _stream(x, stream)))
@@ -296,7 +373,7 @@ def fp8_silu_mul(gu, out=None, stream=None):
         raise ValueError("gu: the column count must be even (gate | up)")
     inner = two_i // 2
     out = torch.empty((rows, inner), dtype=torch.bfloat16, device=gu.device) if out is None else out
-    _need(out, torch.bfloat16, (rows, inner), "out")
+    _need(out, torch.bfloat16, (rows, inner), "out", gu.device)
     _check("fp8_silu_mul", lib().fp8_silu_mul(_ptr(gu), rows, inner, _ptr(out),
                                               _stream(gu, stream)))
     return out
@@ -307,9 +384,9 @@ def fp8_rmsnorm(x, gamma, eps: float = RMS_EPS, out=None, stream=None):
     import torch
     rows, hidden = x.shape
     _need(x, torch.bfloat16, (rows, hidden), "x")
-    _need(gamma, torch.bfloat16, (hidden,), "gamma")
+    _need(gamma, torch.bfloat16, (hidden,), "gamma", x.device)
     out = torch.empty((rows, hidden), dtype=torch.bfloat16, device=x.device) if out is None else out
-    _need(out, torch.bfloat16, (rows, hidden), "out")
+    _need(out, torch.bfloat16, (rows, hidden), "out", x.device)
     _check("fp8_rmsnorm", lib().fp8_rmsnorm(_ptr(x), _ptr(gamma), rows, hidden, float(eps),
                                             _ptr(out), _stream(x, stream)))
     return out
@@ -328,8 +405,10 @@ def fp8_calib_scale(x, lo_permille: int = 1, hi_permille: int = 999, scale=None,
         raise ValueError("x: contiguous bf16 device tensor expected")
     n = x.numel()
     scale = torch.empty((1,), dtype=torch.float32, device=x.device) if scale is None else scale
+    _need(scale, torch.float32, (1,), "scale", x.device)
     need = fp8_calib_workspace_bytes(n)
     ws = torch.empty(need, dtype=torch.uint8, device=x.device) if ws is None else ws
+    _need_ws(ws, x.device)
     _check("fp8_calib_scale", lib().fp8_calib_scale(
         _ptr(x), n, lo_permille, hi_permille, _ptr(scale), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(x, stream)))
@@ -343,6 +422,8 @@ def fp8_quant_static(x, scale, q=None, stream=None):
     if x.dtype != torch.bfloat16 or not x.is_contiguous() or not x.is_cuda:
         raise ValueError("x: contiguous bf16 device tensor expected")
     q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if q is None else q
+    _need(scale, torch.float32, (1,), "scale", x.device)   # read on the device
+    _need(q, torch.uint8, tuple(x.shape), "q", x.device)
     _check("fp8_quant_static", lib().fp8_quant_static(
         _ptr(x), x.numel(), _ptr(scale), _ptr(q), _stream(x, stream)))
     return q
@@ -354,13 +435,14 @@ def fp8_kv_cache_quant(k, v, slots, k_cache, v_cache, k_scale, v_scale, stream=N
     import torch
     T, width = k.shape
     _need(k, torch.bfloat16, (T, width), "k")
-    _need(v, torch.bfloat16, (T, width), "v")
-    _need(slots, torch.int64, (T,), "slots")
+    dev = k.device
+    _need(v, torch.bfloat16, (T, width), "v", dev)
+    _need(slots, torch.int64, (T,), "slots", dev)
     n_slots = k_cache.shape[0]
-    _need(k_cache, torch.uint8, (n_slots, width), "k_cache")
-    _need(v_cache, torch.uint8, (n_slots, width), "v_cache")
-    _need(k_scale, torch.float32, (n_slots,), "k_scale")
-    _need(v_scale, torch.float32, (n_slots,), "v_scale")
+    _need(k_cache, torch.uint8, (n_slots, width), "k_cache", dev)
+    _need(v_cache, torch.uint8, (n_slots, width), "v_cache", dev)
+    _need(k_scale, torch.float32, (n_slots,), "k_scale", dev)
+    _need(v_scale, torch.float32, (n_slots,), "v_scale", dev)
     _check("fp8_kv_cache_quant", lib().fp8_kv_cache_quant(
         _ptr(k), _ptr(v), T, width, _ptr(slots), n_slots, _ptr(k_cache), _ptr(v_cache),
         _ptr(k_scale), _ptr(v_scale), _stream(k, stream)))

@@ -49,6 +49,7 @@
 #include "device_common.hpp"
 #include "kernels.hpp"
 
+#include <atomic>
 #include <mutex>
 
 namespace fp8dq {
@@ -549,12 +550,21 @@ void launch_reg_dec(const uint8_t* qx, const float* sx, const uint8_t* qw,
                      p.kt_per_split);
 }
 
+// CUs of the current device, asked once per device (the plan runs on every
+// call, and a decode linear takes 15-20 us)
 int decode_cu_count() {
+  constexpr int kDevs = 64;
+  static std::atomic<int> cached[kDevs];   // 0: not asked yet
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < kDevs) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       ncu <= 0)
     return 256;
+  if (dev >= 0 && dev < kDevs) cached[dev].store(ncu, std::memory_order_relaxed);
   return ncu;
 }
 

@@ -610,3 +610,42 @@ def test_empty_inputs(F):
     y, qx, sx = F.fp8_linear(x, qw, sw)
     torch.cuda.synchronize()
     assert y.shape == (0, 128)
+
+
+def test_binding_rejects_mismatched_tensors(F):
+    """The binding checks every tensor's dtype, shape, layout and device
+    before its pointer reaches the library (which sees only pointers and
+    sizes): each mismatch raises ValueError and launches nothing."""
+    d = "cuda"
+    M, N, K = 8, 256, 512
+    x = torch.zeros((M, K), dtype=torch.bfloat16, device=d)
+    qx = torch.zeros((M, K), dtype=torch.uint8, device=d)
+    sx = torch.ones(M, dtype=torch.float32, device=d)
+    qw = torch.zeros((N, K), dtype=torch.uint8, device=d)
+    sw = torch.ones(N, dtype=torch.float32, device=d)
+    bad = [
+        lambda: F.fp8_gemm(qx, sx, qw[:, :256].contiguous(), sw),           # W rows of another K
+        lambda: F.fp8_gemm(qx, sx, qw, sw[:128]),                            # too few channel scales
+        lambda: F.fp8_gemm(qx, sx.double(), qw, sw),                         # wrong dtype
+        lambda: F.fp8_gemm(qx, sx, qw.t().contiguous().t(), sw),             # not contiguous
+        lambda: F.fp8_gemm(qx, sx, qw, sw, y=torch.empty((M, N + 1), dtype=torch.bfloat16, device=d)),
+        lambda: F.fp8_gemm(qx, sx, qw, sw, ws=torch.zeros(1 << 20, dtype=torch.uint8)),  # host ws
+        lambda: F.fp8_linear(x, qw, sw.cpu()),                               # host scales
+        lambda: F.fp8_linear(x, qw, sw, qx_out=torch.empty((M, K + 8), dtype=torch.uint8, device=d)),
+        lambda: F.fp8_linear_noalloc(x, qw[:128], sw),                       # W and scales disagree
+        lambda: F.fp8_gemm_block(qx, torch.ones((M, 4), device=d), qw[:200].contiguous(),
+                                 torch.ones((2, 4), device=d)),              # N not a multiple of 128
+        lambda: F.fp8_linear_block(x, qw, torch.ones((2, 3), device=d)),    # wrong block-scale grid
+        lambda: F.fp8_quant_act(x, group=64),
+        lambda: F.fp8_quant_static(x, torch.ones(1)),                        # scale read on the device
+        lambda: F.fp8_rmsnorm_quant(x, torch.ones(K + 8, dtype=torch.bfloat16, device=d)),
+        lambda: F.fp8_kv_cache_quant(x, x, torch.zeros(M, dtype=torch.int32, device=d),
+                                     torch.zeros((16, K), dtype=torch.uint8, device=d),
+                                     torch.zeros((16, K), dtype=torch.uint8, device=d),
+                                     torch.zeros(16, device=d), torch.zeros(16, device=d)),
+    ]
+    for i, f in enumerate(bad):
+        with pytest.raises(ValueError):
+            f()
+            pytest.fail(f"case {i} was not rejected")
+    torch.cuda.synchronize()
