@@ -201,3 +201,33 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _binding.lib()
+
+
+def test_binding_tensor_checks():
+    """The binding's per-tensor check (before any pointer reaches the
+    library): dtype, shape, layout and device; block shapes need N and K
+    multiples of 128 (host logic only, so host tensors stand in)."""
+    import torch
+    from fp8_dynamic_quantized_amd import _binding
+    need = _binding._need
+    t = torch.zeros((4, 8), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="expected"):
+        need(t, torch.float32, (4, 8), "t")                     # dtype
+    with pytest.raises(ValueError, match="expected"):
+        need(t, torch.uint8, (4, 16), "t")                      # shape
+    with pytest.raises(ValueError, match="expected"):
+        need(t.t(), torch.uint8, (8, 4), "t")                   # not contiguous
+    with pytest.raises(ValueError, match="device memory"):
+        need(t, torch.uint8, (4, 8), "t")                       # host memory
+    with pytest.raises(ValueError, match="missing"):
+        need(None, torch.uint8, (4, 8), "t")
+    with pytest.raises(ValueError, match="multiples of 128"):
+        _binding._need_blocks(200, 512)
+    with pytest.raises(ValueError, match="multiples of 128"):
+        _binding._need_blocks(256, 320)
+    _binding._need_blocks(256, 512)
+    with pytest.raises(ValueError, match="contiguous device memory"):
+        _binding._need_ws(torch.zeros(16, dtype=torch.uint8), torch.device("cuda", 0))
+    with pytest.raises(ValueError, match="multiples of 128"):
+        F.fp8_gemm_block(torch.zeros((8, 512), dtype=torch.uint8), torch.ones((8, 4)),
+                         torch.zeros((200, 512), dtype=torch.uint8), torch.ones((2, 4)))
