@@ -8,7 +8,7 @@ measured accumulation law of the FP8 matrix instructions (tests/mfma_law.py).
 * The longest rows the boundary accepts (K = FP8DQ_MAX_K = 131072): decode
   within the tolerance of the oracle; prefill within the tolerance of the
   law's prediction (and the nominal tolerance counted).
-* Every output of the 70B decode o and down linears at 1 and 64 tokens
+* Every output of the four 70B decode linears at 1, 8, 32 and 64 tokens
   within the tolerance of the oracle.
 * Per-channel scales near both ends of the fp32 range on every kernel path:
   finite outputs, within the tolerance of the law's prediction.
@@ -203,17 +203,18 @@ def test_decode_workspace_reuse(F):
         assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), f"call {i}"
 
 
-@pytest.mark.parametrize("j", [1, 3])
+@pytest.mark.parametrize("j", [0, 1, 2, 3])
 def test_c3_every_output(F, j):
-    """70B decode o (j = 1) and down (j = 3) at 1 and 64 tokens: every output
-    of the linear within tolerance of the oracle."""
+    """70B decode qkv, o, gate_up and down (j = 0..3) at 1, 8, 32 and 64
+    tokens (both decode kernels, every token-row layout): every output of
+    the linear within tolerance of the oracle."""
     d = synth.workload(3, j, 3)
     K, N = d["K"], d["N"]
     say(f"c3 every output {d['name']} {N}x{K}")
     qw_o, sw_o = O.quant_per_row(d["w"])
     vw = O.e4m3_decode(qw_o)
     qw_d, sw_d = dev(qw_o), dev(sw_o)
-    for M in (1, 64):
+    for M in (1, 8, 32, 64):
         xb = d["x"][:M]
         qx_o, sx_o = O.quant_per_row(xb)
         y, qx, sx = F.fp8_linear(dev_bf16(xb), qw_d, sw_d)
