@@ -428,3 +428,31 @@ def test_rmsnorm_subnormal_intermediate(F):
     qo, so = O.rmsnorm_quant(x, gamma)
     assert_scales_equal(s.cpu().numpy(), so, "subnormal-intermediate scales")
     assert_codes_equal(q.cpu().numpy(), qo, "subnormal-intermediate codes")
+
+
+@pytest.mark.parametrize("eps", [1e-30, 0.5, 1e30])
+def test_rmsnorm_eps_range(F, eps):
+    """eps at both ends of the accepted range [1e-30, 1e30] and between, on
+    rows that make it matter: an all-zero row, rows of tiny and of
+    bf16-subnormal values, an ordinary row and one near the bf16 maximum.
+    bf16 h and codes bit-exact."""
+    rows, hidden = 8, 1024
+    rng = np.random.default_rng(int(np.log10(eps)) + 200)
+    xf = rng.normal(0.0, 1.0, (rows, hidden))
+    xf[1] = 0.0
+    xf[2] *= 1e-36                                    # tiny normal values
+    xf[3] = rng.integers(1, 128, hidden) * 2.0 ** -133 * rng.choice([-1.0, 1.0], hidden)
+    xf[4] *= 1e35                                     # near the bf16 maximum
+    x = bits_of(xf)
+    gamma = bits_of(rng.normal(1.0, 0.3, hidden))
+    say(f"rmsnorm eps={eps}")
+    want = O.rmsnorm_bf16(x, gamma, eps)
+    h = F.fp8_rmsnorm(dev_bf16(x), dev_bf16(gamma), eps=eps)
+    q, s = F.fp8_rmsnorm_quant(dev_bf16(x), dev_bf16(gamma), eps=eps)
+    torch.cuda.synchronize()
+    got = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    bad = np.flatnonzero(got.ravel() != want.ravel())
+    assert bad.size == 0, f"{bad.size} h mismatches, first at {bad[:5]}"
+    qo, so = O.rmsnorm_quant(x, gamma, eps)
+    assert_scales_equal(s.cpu().numpy(), so, "eps-range scales")
+    assert_codes_equal(q.cpu().numpy(), qo, "eps-range codes")
