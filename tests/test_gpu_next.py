@@ -189,7 +189,10 @@ def test_quant_static(F, n, scale):
 
 
 @pytest.mark.parametrize("T,width,n_slots", [(37, 1024, 64), (5, 8, 8), (300, 1024, 512),
-                                             (16, 8192, 20)])
+                                             (16, 8192, 20),
+                                             # every rung of the row-team ladder
+                                             (64, 2048, 100), (9, 4096, 12),
+                                             (5, 16384, 7), (3, 65536, 8)])
 def test_kv_cache_quant(F, T, width, n_slots):
     say(f"kv cache T={T} width={width} slots={n_slots}")
     k = synth.activations(T, width, 9000 + T, 9001)
