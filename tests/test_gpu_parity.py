@@ -37,7 +37,11 @@ def sample_idx(n, k, seed):
 # ----------------------------------------------------------------------------
 ROW_SHAPES = [(1, 8), (3, 40), (5, 512), (7, 520), (64, 4096), (33, 3072),
               (17, 8192), (9, 14336), (5, 28672), (3, 40960), (2, 65536),
-              (130, 1024), (300, 2056), (129, 3000), (200, 4096), (140, 14336), (130, 16384)]
+              (130, 1024), (300, 2056), (129, 3000), (200, 4096), (140, 14336), (130, 16384),
+              # the many-row ladder's other rungs (1 to 16 chunks per lane, 1 to 8
+              # waves per row) and the two-pass kernel
+              (129, 512), (131, 2048), (132, 6144), (133, 8192), (134, 12288),
+              (135, 24576), (136, 32768), (137, 40960)]
 
 
 @pytest.mark.parametrize("rows,K", ROW_SHAPES)
