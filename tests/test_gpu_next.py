@@ -39,7 +39,9 @@ def gate_up(rows, inner, seed, extreme=True):
     return gu
 
 
-SILU_SHAPES = [(1, 8), (3, 136), (64, 1024), (17, 14336), (5, 28672), (130, 512), (2, 65536)]
+SILU_SHAPES = [(1, 8), (3, 136), (64, 1024), (17, 14336), (5, 28672), (130, 512), (2, 65536),
+               # every rung of the row-team ladder (4 waves, 2 to 8 chunks per lane)
+               (6, 4096), (7, 6144), (9, 8192), (4, 10240), (3, 12288), (5, 16384)]
 
 
 @pytest.mark.parametrize("rows,inner", SILU_SHAPES)
@@ -77,7 +79,9 @@ def norm_input(rows, hidden, seed):
     return bits_of(xf), gamma
 
 
-RMS_SHAPES = [(1, 8), (5, 4096), (64, 4096), (7, 8192), (3, 16384), (130, 512), (2, 65536)]
+RMS_SHAPES = [(1, 8), (5, 4096), (64, 4096), (7, 8192), (3, 16384), (130, 512), (2, 65536),
+              # the ladder's other rungs
+              (6, 6144), (4, 10240), (3, 12288), (5, 14336), (2, 28672)]
 
 
 @pytest.mark.parametrize("rows,hidden", RMS_SHAPES)
